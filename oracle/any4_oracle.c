@@ -1,0 +1,389 @@
+/*
+ * any4 quantizer: CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path (the HIP
+ * library under weight_only_bit_row_amd/) shares no code, header, table or
+ * constant with this file.
+ *
+ * Plain, single-threaded, slow on purpose: every step is written out the way
+ * "any4: Learned 4-bit Numeric Representation for LLMs" (arXiv 2507.04610) states
+ * it, so that a reader can check it against the paper by eye.  Build with
+ * -O2 -ffp-contract=off so that no multiply-add is fused.
+ *
+ * Precision: the scaled weights (Section 2.5.1, Eq. 1-2), the sample weights,
+ * the squared distances of the E-step (Section 4.1, Eq. 18) and the k-means++
+ * sampling weights are fp32, because they decide integers (codes, picks) and
+ * both sides must take those decisions in the same precision.  The M-step sums
+ * (Eq. 23) and the objective are fp64.
+ *
+ * Pinned by tests/test_oracle_*.py (closed forms, brute-force / DP optimum,
+ * scikit-learn Lloyd, numpy Philox4x64, numpy float16 casts, the storage cost
+ * printed in Section 2.4.1).  Philox4x32-10's round constants are pinned only
+ * through the shared round structure (Philox4x64-10 vs numpy) and a uniformity
+ * test: its absolute stream is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_INVALID_ARG 1
+#define ORACLE_ERR_NONFINITE 5
+
+/* Sample weights above this bound are rejected together with non-finite values, so
+ * that fp32 sums over a row can never overflow (2^64 * 15 * 2^22 < 2^128). */
+#define ORACLE_A_MAX 18446744073709551616.0f /* 2^64 */
+
+int oracle_any4_version(void) { return 1; }
+
+/* ------------------------------------------------------------------------- */
+/* Philox-4xW-10, from Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+ * as easy as 1, 2, 3" (SC'11), Section 4.  One round multiplies words 0 and 2 by
+ * the two round multipliers, then forms the new 4-word state from the products'
+ * high halves xor-ed with the other two words and the round key, and from the
+ * products' low halves.  The key is bumped by the two Weyl constants between
+ * rounds.  The 64-bit variant (checked against numpy.random.Philox) and the
+ * 32-bit variant share this structure through one macro. */
+
+static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
+    uint64_t p = (uint64_t)a * (uint64_t)b;
+    *hi = (uint32_t)(p >> 32);
+    *lo = (uint32_t)p;
+}
+
+static inline void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
+    unsigned __int128 p = (unsigned __int128)a * (unsigned __int128)b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+#define PHILOX4_ROUNDS(T, MULHILO, M0, M1, W0, W1, ctr, key, out)            \
+    do {                                                                     \
+        T x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];                \
+        T k0 = key[0], k1 = key[1];                                          \
+        for (int round = 0; round < 10; ++round) {                           \
+            if (round > 0) { k0 += (T)(W0); k1 += (T)(W1); }                 \
+            T hi0, lo0, hi1, lo1;                                            \
+            MULHILO((T)(M0), x0, &hi0, &lo0);                                \
+            MULHILO((T)(M1), x2, &hi1, &lo1);                                \
+            T y0 = hi1 ^ x1 ^ k0;                                            \
+            T y1 = lo1;                                                      \
+            T y2 = hi0 ^ x3 ^ k1;                                            \
+            T y3 = lo0;                                                      \
+            x0 = y0; x1 = y1; x2 = y2; x3 = y3;                              \
+        }                                                                    \
+        out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;                  \
+    } while (0)
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    PHILOX4_ROUNDS(uint32_t, mulhilo32, 0xD2511F53u, 0xCD9E8D57u, 0x9E3779B9u, 0xBB67AE85u,
+                   ctr, key, out);
+}
+
+void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+    PHILOX4_ROUNDS(uint64_t, mulhilo64, 0xD2E7470EE14C6C93ull, 0xCA5A826395121157ull,
+                   0x9E3779B97F4A7C15ull, 0xBB67AE8584CAA73Bull, ctr, key, out);
+}
+
+/* ------------------------------------------------------------------------- */
+/* IEEE binary16 with round-to-nearest-even, from the binary32 bit pattern.
+ * The LUT is stored as 16 fp16 values and each group as two fp16 values
+ * (OpenReview rebuttal; Section 2.4.1 of the paper). */
+static uint16_t fp16_rne(float f) {
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    uint32_t e = (x >> 23) & 0xFFu;
+    uint32_t m = x & 0x7FFFFFu;
+    if (e == 0xFFu) {                       /* inf or nan */
+        if (m == 0) return (uint16_t)(sign | 0x7C00u);
+        return (uint16_t)(sign | 0x7E00u | (m >> 13));
+    }
+    int32_t exp = (int32_t)e - 127;         /* unbiased */
+    if (exp > 15) return (uint16_t)(sign | 0x7C00u);   /* overflow: > 65504 range */
+    if (exp >= -14) {                       /* normal fp16 range */
+        uint32_t mant = m;                  /* 23 bits, keep 10 */
+        uint32_t keep = mant >> 13;
+        uint32_t rest = mant & 0x1FFFu;
+        uint32_t h = ((uint32_t)(exp + 15) << 10) | keep;
+        if (rest > 0x1000u || (rest == 0x1000u && (keep & 1u))) h += 1;  /* may carry into exp */
+        return (uint16_t)(sign | h);        /* carry into 0x7C00 gives inf, as it should */
+    }
+    /* subnormal fp16 (or underflow to zero): value = mant24 * 2^(exp-23),
+     * fp16 subnormal unit is 2^-24, so the count is mant24 * 2^(exp-23+24). */
+    if (e == 0) return (uint16_t)sign;      /* fp32 zero or subnormal: far below 2^-25 */
+    uint32_t mant24 = m | 0x800000u;
+    int32_t shift = -(exp + 1);             /* right shift so that unit = 2^-24 */
+    /* exp in [-127+1, -15]: shift in [14, 126] */
+    if (shift > 24 + 1) return (uint16_t)sign;
+    uint32_t keep = mant24 >> shift;
+    uint32_t rest = mant24 & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rest > half || (rest == half && (keep & 1u))) keep += 1;
+    return (uint16_t)(sign | keep);         /* keep == 0x400 becomes the smallest normal */
+}
+
+uint16_t oracle_fp16_rne(float f) { return fp16_rne(f); }
+
+void oracle_fp16_rne_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = fp16_rne(in[i]);
+}
+
+static float bf16_to_f32(uint16_t b) {
+    uint32_t x = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &x, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Step 1: group-wise asymmetric min/max scaling, Section 2.5.1 Eq. 1 and Eq. 2.
+ * Groups are g contiguous elements of the row, t*g <= j < (t+1)*g (the paper
+ * prints the range as kg <= j < k(g+1); the corrected range is used).
+ * alpha = (max - min) / (Qmax - Qmin) with Qmax - Qmin = 2^n - 1, beta = min,
+ * w_S = (w - beta) / alpha.  A constant group (alpha = 0) gets w_S = 0.
+ * Returns 0, or 1 when a value or alpha is not finite. */
+int oracle_scale_row(const float* w, int64_t K, int32_t group, int32_t qr,
+                     float* ws, float* alpha, float* beta) {
+    int bad = 0;
+    for (int64_t t = 0; t < K / group; ++t) {
+        const float* wg = w + t * group;
+        float mn = wg[0], mx = wg[0];
+        for (int64_t j = 0; j < group; ++j) {
+            if (!isfinite(wg[j])) bad = 1;
+            if (wg[j] < mn) mn = wg[j];
+            if (wg[j] > mx) mx = wg[j];
+        }
+        float range = mx - mn;
+        float al = range / (float)qr;
+        if (!isfinite(al)) bad = 1;
+        alpha[t] = al;
+        beta[t] = mn;
+        for (int64_t j = 0; j < group; ++j) {
+            if (al > 0.0f) {
+                float diff = wg[j] - mn;
+                ws[t * group + j] = diff / al;
+            } else {
+                ws[t * group + j] = 0.0f;
+            }
+        }
+    }
+    return bad;
+}
+
+/* Step 2: the per-element sample weight of Eq. 23, alpha_{i,j} * E|x_j|, in fp32.
+ * Returns 1 when an activation statistic is negative or not finite, or a weight
+ * is not finite or above the bound. */
+int oracle_weights_row(const float* alpha, const float* act, int64_t K, int32_t group, float* a) {
+    int bad = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        if (!isfinite(act[j]) || act[j] < 0.0f) bad = 1;
+        a[j] = alpha[j / group] * act[j];
+        if (!isfinite(a[j]) || a[j] > ORACLE_A_MAX) bad = 1;
+    }
+    return bad;
+}
+
+static float sqdist(float x, float c) {
+    float d = x - c;
+    return d * d;
+}
+
+/* Step 3: weighted k-means++ seeding (D^2 sampling, Arthur and Vassilvitskii 2007,
+ * which the paper's Appendix C.2 names as scikit-learn's default init).  The
+ * first centre is drawn with probability proportional to the sample weight a_j,
+ * every later one proportional to a_j * D_j, where D_j is the squared distance to
+ * the nearest centre drawn so far.
+ *
+ * Sampling is done exactly in integers: with M = max_j p_j and e = floor(log2 M),
+ * q_j = floor(p_j * 2^(40-e)) (so q_j < 2^41), Q = sum q_j, and one Philox4x32-10
+ * draw per (row, t): u = x1 * 2^32 + x0 with counter (lo32(row), t, matrix,
+ * hi32(row)) and key (lo32(seed), hi32(seed)); r = floor(u * Q / 2^64); the pick is
+ * the smallest j whose prefix sum of q exceeds r.  When every p_j is 0 the centre
+ * is copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1. */
+int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
+                    uint64_t seed, uint64_t row_id, uint32_t matrix_index,
+                    float* c0, int32_t* picks) {
+    float* D = (float*)malloc((size_t)K * sizeof(float));
+    float* p = (float*)malloc((size_t)K * sizeof(float));
+    uint64_t* q = (uint64_t*)malloc((size_t)K * sizeof(uint64_t));
+    if (!D || !p || !q) { free(D); free(p); free(q); return ORACLE_ERR_INVALID_ARG; }
+
+    for (int32_t t = 0; t < k; ++t) {
+        float M = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            p[j] = (t == 0) ? a[j] : a[j] * D[j];
+            if (p[j] > M) M = p[j];
+        }
+        if (M == 0.0f) {
+            c0[t] = (t == 0) ? ws[0] : c0[0];
+            picks[t] = -1;
+        } else {
+            int E;
+            frexp((double)M, &E);               /* M = f * 2^E, f in [0.5, 1) */
+            int e = E - 1;                       /* floor(log2 M) */
+            uint64_t Q = 0;
+            for (int64_t j = 0; j < K; ++j) {
+                double v = ldexp((double)p[j], 40 - e);
+                q[j] = (uint64_t)floor(v);
+                Q += q[j];
+            }
+            uint32_t ctr[4] = {(uint32_t)row_id, (uint32_t)t, matrix_index,
+                               (uint32_t)(row_id >> 32)};
+            uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+            uint32_t x[4];
+            oracle_philox4x32_10(ctr, key, x);
+            uint64_t u = ((uint64_t)x[1] << 32) | (uint64_t)x[0];
+            uint64_t r = (uint64_t)(((unsigned __int128)u * (unsigned __int128)Q) >> 64);
+            uint64_t prefix = 0;
+            int64_t pick = K - 1;
+            for (int64_t j = 0; j < K; ++j) {
+                prefix += q[j];
+                if (prefix > r) { pick = j; break; }
+            }
+            c0[t] = ws[pick];
+            picks[t] = (int32_t)pick;
+        }
+        for (int64_t j = 0; j < K; ++j) {
+            float d = sqdist(ws[j], c0[t]);
+            if (t == 0 || d < D[j]) D[j] = d;
+        }
+    }
+    free(D); free(p); free(q);
+    return ORACLE_OK;
+}
+
+/* Step 4a: E-step, Section 4.1 Eq. 18: each scaled weight goes to the LUT value
+ * with the smallest squared distance; on equal distances the lowest index wins. */
+void oracle_estep_row(const float* ws, int64_t K, const float* c, int32_t k, uint8_t* q) {
+    for (int64_t j = 0; j < K; ++j) {
+        int best = 0;
+        float bd = sqdist(ws[j], c[0]);
+        for (int t = 1; t < k; ++t) {
+            float d = sqdist(ws[j], c[t]);
+            if (d < bd) { bd = d; best = t; }
+        }
+        q[j] = (uint8_t)best;
+    }
+}
+
+/* Step 4b: M-step, Section 4.1 Eq. 23: each LUT value becomes the mean of its
+ * cluster's scaled weights weighted by alpha_{i,j} * E|x_j|.  A cluster whose
+ * weight sum is 0 keeps its previous value. */
+void oracle_mstep_row(const float* ws, const float* a, const uint8_t* q, int64_t K,
+                      const float* c_prev, int32_t k, float* c_new) {
+    double S1[16], S0[16];
+    for (int t = 0; t < k; ++t) { S1[t] = 0.0; S0[t] = 0.0; }
+    for (int64_t j = 0; j < K; ++j) {
+        S1[q[j]] += (double)a[j] * (double)ws[j];
+        S0[q[j]] += (double)a[j];
+    }
+    for (int t = 0; t < k; ++t)
+        c_new[t] = (S0[t] > 0.0) ? (float)(S1[t] / S0[t]) : c_prev[t];
+}
+
+/* The weighted objective that the E/M alternation decreases:
+ * J = sum_j a_j (w_S_j - c_{q_j})^2, in fp64. */
+double oracle_objective_row(const float* ws, const float* a, const uint8_t* q, int64_t K,
+                            const float* c) {
+    double J = 0.0;
+    for (int64_t j = 0; j < K; ++j) {
+        double d = (double)ws[j] - (double)c[q[j]];
+        J += (double)a[j] * d * d;
+    }
+    return J;
+}
+
+/* Step 6: codes, two per byte, the even column in the low nibble. */
+void oracle_pack_row(const uint8_t* q, int64_t K, uint8_t* codes) {
+    for (int64_t m = 0; m < K / 2; ++m)
+        codes[m] = (uint8_t)((q[2 * m] & 0xF) | ((q[2 * m + 1] & 0xF) << 4));
+}
+
+/* ------------------------------------------------------------------------- */
+/* The whole path for rows [0, n_rows) of one matrix, row-major.
+ * Per row (Algorithm 1 of the paper's Appendix A, minus the calibration and the
+ * module loop): scale, weights, k-means++ seed, `iters` rounds of E-step then
+ * M-step, a final E-step, then emission (fp16 LUT in draw order, fp16 alpha and
+ * beta, nibble-packed codes).  Traces are optional (NULL to skip):
+ *   c_trace [n_rows, iters+1, k]  centroids c^0 .. c^iters
+ *   j_trace [n_rows, iters+1]     J at c^0 .. c^iters, each with the E-step
+ *                                 assignment at those centroids
+ *   picks   [n_rows, k]           k-means++ picks
+ *   c_final [n_rows, k]           fp32 centroids before the fp16 cast
+ * A row with a non-finite input, a negative activation statistic, a non-finite
+ * alpha or a too-large weight gets zero outputs and a NaN objective, and the call
+ * returns ORACLE_ERR_NONFINITE after finishing the other rows. */
+int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n_cols,
+                         const float* act, int64_t row_offset, int32_t matrix_index,
+                         int32_t group, int32_t n_clusters, int32_t iters, uint64_t seed,
+                         uint8_t* codes, uint16_t* lut, uint16_t* scale, uint16_t* offset,
+                         double* objective, float* c_trace, double* j_trace,
+                         int32_t* picks, float* c_final) {
+    const int64_t K = n_cols;
+    const int32_t k = n_clusters;
+    if (n_rows < 0 || K < 2 || (K & 1) || group < 1 || K % group != 0 || iters < 0 ||
+        (dtype != 0 && dtype != 1) || row_offset < 0 ||
+        !(k == 2 || k == 4 || k == 8 || k == 16))
+        return ORACLE_ERR_INVALID_ARG;
+    const int32_t qr = k - 1;
+    const int64_t G = K / group;
+    float* wrow = (float*)malloc((size_t)K * sizeof(float));
+    float* ws = (float*)malloc((size_t)K * sizeof(float));
+    float* a = (float*)malloc((size_t)K * sizeof(float));
+    float* alpha = (float*)malloc((size_t)G * sizeof(float));
+    float* beta = (float*)malloc((size_t)G * sizeof(float));
+    uint8_t* q = (uint8_t*)malloc((size_t)K);
+    if (!wrow || !ws || !a || !alpha || !beta || !q) {
+        free(wrow); free(ws); free(a); free(alpha); free(beta); free(q);
+        return ORACLE_ERR_INVALID_ARG;
+    }
+    int status = ORACLE_OK;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        if (dtype == 0) {
+            memcpy(wrow, (const float*)w + i * K, (size_t)K * sizeof(float));
+        } else {
+            const uint16_t* wb = (const uint16_t*)w + i * K;
+            for (int64_t j = 0; j < K; ++j) wrow[j] = bf16_to_f32(wb[j]);
+        }
+        int bad = oracle_scale_row(wrow, K, group, qr, ws, alpha, beta);
+        bad |= oracle_weights_row(alpha, act, K, group, a);
+        for (int64_t j = 0; j < K && !bad; ++j)
+            if (!isfinite(a[j] * ws[j])) bad = 1;
+        if (bad) {
+            status = ORACLE_ERR_NONFINITE;
+            memset(codes + i * (K / 2), 0, (size_t)(K / 2));
+            memset(lut + i * k, 0, (size_t)k * 2);
+            memset(scale + i * G, 0, (size_t)G * 2);
+            memset(offset + i * G, 0, (size_t)G * 2);
+            if (objective) objective[i] = NAN;
+            continue;
+        }
+        float c[16], cn[16];
+        int32_t pk[16];
+        oracle_seed_row(ws, a, K, k, seed, (uint64_t)(row_offset + i), (uint32_t)matrix_index,
+                        c, pk);
+        if (picks) memcpy(picks + i * k, pk, (size_t)k * sizeof(int32_t));
+        for (int32_t it = 0; it <= iters; ++it) {
+            oracle_estep_row(ws, K, c, k, q);
+            if (c_trace) memcpy(c_trace + (i * (iters + 1) + it) * k, c, (size_t)k * sizeof(float));
+            if (j_trace) j_trace[i * (iters + 1) + it] = oracle_objective_row(ws, a, q, K, c);
+            if (it == iters) break;
+            oracle_mstep_row(ws, a, q, K, c, k, cn);
+            memcpy(c, cn, sizeof(c));
+        }
+        /* q now holds the final E-step at c^iters */
+        if (objective) objective[i] = oracle_objective_row(ws, a, q, K, c);
+        if (c_final) memcpy(c_final + i * k, c, (size_t)k * sizeof(float));
+        oracle_pack_row(q, K, codes + i * (K / 2));
+        for (int t = 0; t < k; ++t) lut[i * k + t] = fp16_rne(c[t]);
+        for (int64_t g = 0; g < G; ++g) {
+            scale[i * G + g] = fp16_rne(alpha[g]);
+            offset[i * G + g] = fp16_rne(beta[g]);
+        }
+    }
+    free(wrow); free(ws); free(a); free(alpha); free(beta); free(q);
+    return status;
+}
