@@ -1,0 +1,154 @@
+/*
+ * any4.h: C ABI of the MI355X (gfx950) any4 quantizer.
+ *
+ * The operation is the per-row quantizer of "any4: Learned 4-bit Numeric
+ * Representation for LLMs" (arXiv 2507.04610): group-wise asymmetric min/max
+ * scaling of each weight row (Section 2.5.1, Eq. 1-2), a LUT of 2^n values per
+ * row learned by weighted k-means on the scaled row, with sample weights
+ * alpha_{i,j} * E|x_j| (Section 4.1: E-step Eq. 18, M-step Eq. 23; k-means++
+ * initialisation per Appendix C.2), and storage as n-bit codes plus an fp16 LUT
+ * per row and an fp16 scale and offset per group (Section 2.4.1).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers unless stated otherwise; every call
+ *    is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *  - The caller allocates and owns every buffer, including the workspace; the
+ *    library never allocates device memory and keeps no mutable global state,
+ *    so concurrent calls on different streams are safe.
+ *  - Argument validation is synchronous and happens before any launch: on a
+ *    validation error nothing is launched and no output is written.
+ *  - Return value: an ANY4_* status; no C++ exception crosses the ABI.
+ *  - Layouts are row-major and contiguous.
+ *  - Results are a pure function of (W, act_absmean, params, row_offset,
+ *    matrix_index): repeat runs are bit-identical, and quantizing rows
+ *    [r0, r0 + n) with row_offset = r0 gives the same bits as those rows of a
+ *    whole-matrix call.
+ */
+#ifndef ANY4_H
+#define ANY4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+/* element type of W */
+enum { ANY4_F32 = 0, ANY4_BF16 = 1 };
+
+/* status codes */
+enum {
+  ANY4_OK = 0,
+  ANY4_ERR_INVALID_ARG = 1,  /* bad pointer, size, group, cluster count, ... */
+  ANY4_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle (e.g. K > 32768) */
+  ANY4_ERR_WORKSPACE = 3,    /* workspace missing or smaller than any4_workspace_bytes() */
+  ANY4_ERR_HIP = 4,          /* a HIP launch failed (hipGetLastError) */
+  ANY4_ERR_NONFINITE = 5     /* device-detected bad row, read with any4_read_device_status() */
+};
+
+/* One weight matrix and its outputs.
+ *   w            [n_rows, n_cols] of w_dtype (fp32, or bf16 bits as uint16)
+ *   act_absmean  [n_cols] fp32, E|x_j| per input channel (Section 4.1, calibration
+ *                statistic); must be finite and >= 0
+ *   row_offset   added to the row index in the Philox counter; use it when a
+ *                matrix is quantized in row shards
+ *   matrix_index a Philox counter word; give each matrix of a batch its own
+ *   codes        out [n_rows, n_cols/2] uint8: byte m = q[2m] | q[2m+1] << 4
+ *   lut          out [n_rows, n_clusters] IEEE fp16 bits, centroids in draw order
+ *   scale        out [n_rows, n_cols/group] fp16 alpha (Eq. 2)
+ *   offset       out [n_rows, n_cols/group] fp16 beta = group minimum (Eq. 2)
+ *   objective    out [n_rows] fp64 J = sum_j a_j (w_S_j - lut_q_j)^2 with the
+ *                fp32 centroids, or NULL
+ * A row whose W or E|x| holds a non-finite value, whose E|x| has a negative entry,
+ * or whose alpha or sample weight alpha*E|x| is non-finite or above 2^64, gets
+ * all-zero codes/lut/scale/offset and a NaN objective, and sets ANY4_ERR_NONFINITE
+ * in the workspace status word. */
+typedef struct {
+  const void* w;
+  int32_t w_dtype;
+  int32_t matrix_index;
+  int64_t n_rows;
+  int64_t n_cols;
+  const float* act_absmean;
+  int64_t row_offset;
+  uint8_t* codes;
+  uint16_t* lut;
+  uint16_t* scale;
+  uint16_t* offset;
+  double* objective;
+} any4_matrix;
+
+/* group:      power of two, 2 <= group, n_cols % group == 0 (Section 2.5.1; 128 is
+ *             the paper's default)
+ * n_clusters: 2, 4, 8 or 16 (any1..any4; Qmax - Qmin = n_clusters - 1)
+ * iters:      Lloyd rounds (E-step then M-step), >= 0, followed by one final E-step
+ * seed:       Philox4x32-10 key for k-means++ */
+typedef struct {
+  int32_t group;
+  int32_t n_clusters;
+  int32_t iters;
+  int32_t reserved; /* must be 0 */
+  uint64_t seed;
+} any4_params;
+
+/* Size of the workspace any4_quantize needs for this batch (a device status word
+ * and padding).  Validates the arguments like any4_quantize. */
+int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_params* params,
+                         size_t* bytes_out);
+
+/* Quantize `count` matrices (host array of descriptors) in one call: every row of
+ * every matrix is scaled, seeded with k-means++, refined by `iters` Lloyd rounds,
+ * finally assigned, and emitted.  Per matrix, n_cols must be even and at most
+ * 32768; n_rows may be 0.  The workspace (device, >= any4_workspace_bytes) holds
+ * the status word; it is cleared by this call. */
+int any4_quantize(const any4_matrix* mats, int32_t count, const any4_params* params,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronizes `stream`, then returns the status word a previous any4_quantize
+ * left in `workspace` (ANY4_OK or ANY4_ERR_NONFINITE), or ANY4_ERR_HIP. */
+int any4_read_device_status(const void* workspace, hipStream_t stream);
+
+/* Static English text for a status code. */
+const char* any4_status_string(int status);
+
+/* ---- stage entry points: the same device code as any4_quantize, stopped after
+ * one step, for parity tests against the CPU oracle.  One matrix each; the
+ * any4_matrix output fields that a stage does not produce are ignored. ---- */
+
+/* Eq. 1-2 scaling and Eq. 23 sample weights: w_s [N,K] fp32 scaled row,
+ * alpha/beta [N, K/group] fp32, a [N,K] fp32 = alpha_{g(j)} * E|x_j|. */
+int any4_stage_scale(const any4_matrix* m, const any4_params* params, float* w_s,
+                     float* alpha, float* beta, float* a, hipStream_t stream);
+
+/* Scaling then k-means++ (Appendix C.2): c0 [N, n_clusters] fp32 initial
+ * centroids in draw order, picks [N, n_clusters] int32 column of each draw
+ * (-1 when all sampling weights were 0 and the centre was copied). */
+int any4_stage_seed(const any4_matrix* m, const any4_params* params, float* c0,
+                    int32_t* picks, hipStream_t stream);
+
+/* Scaling, then ONE Lloyd round from the given centroids c_in [N, n_clusters]:
+ * assign [N,K] uint8 E-step result (Eq. 18, lowest index on ties), c_out
+ * [N, n_clusters] M-step result (Eq. 23; an empty cluster keeps its value),
+ * objective [N] fp64 J at c_in with that assignment (may be NULL). */
+int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const float* c_in,
+                          uint8_t* assign, float* c_out, double* objective, hipStream_t stream);
+
+/* Emission only: codes, lut, scale, offset of `m` from assign [N,K] uint8,
+ * c [N, n_clusters] fp32, alpha/beta [N, K/group] fp32 (Section 2.4.1 layout). */
+int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8_t* assign,
+                    const float* c, const float* alpha, const float* beta, hipStream_t stream);
+
+/* The full path like any4_quantize for one matrix, additionally writing the fp32
+ * centroids before the fp16 cast, c_final [N, n_clusters], and the k-means++
+ * picks [N, n_clusters] (either may be NULL). */
+int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_final,
+                    int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ANY4_H */

@@ -1,0 +1,139 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function that
+include/any4.h declares, the ctypes structs match the header layout, and argument
+validation rejects bad calls before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_only_bit_row_amd as any4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "any4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(any4.LIB_PATH):
+        from weight_only_bit_row_amd import build
+        build.build()
+    return any4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(any4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    out = subprocess.run(["nm", "-D", "--defined-only", any4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(any4_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(any4.EXPORTED) == names
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "any4.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(any4_matrix),"
+        " offsetof(any4_matrix, act_absmean), offsetof(any4_matrix, objective),"
+        " sizeof(any4_params), offsetof(any4_params, seed), offsetof(any4_matrix, row_offset));"
+        "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals == [ctypes.sizeof(any4.Any4Matrix), any4.Any4Matrix.act_absmean.offset,
+                    any4.Any4Matrix.objective.offset, ctypes.sizeof(any4.Any4Params),
+                    any4.Any4Params.seed.offset, any4.Any4Matrix.row_offset.offset]
+
+
+def _mat(n=4, k=512, dtype=1):
+    m = any4.Any4Matrix()
+    m.w, m.act_absmean = 0x1000, 0x2000          # never dereferenced on these paths
+    m.codes, m.lut, m.scale, m.offset = 0x3000, 0x4000, 0x5000, 0x6000
+    m.w_dtype, m.n_rows, m.n_cols = dtype, n, k
+    return m
+
+
+def _ws_bytes(L, m, p):
+    out = ctypes.c_size_t(0)
+    st = L.any4_workspace_bytes(ctypes.byref(m), 1, ctypes.byref(p), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_query_and_validation(L):
+    p = any4.params(128, 16, 20, 0)
+    st, nbytes = _ws_bytes(L, _mat(), p)
+    assert st == 0 and nbytes >= 4
+    bad = [
+        (dict(), dict(group=96)),          # not a power of two
+        (dict(), dict(group=1)),
+        (dict(), dict(n_clusters=3)),
+        (dict(), dict(iters=-1)),
+        (dict(k=500), dict()),             # K % group != 0
+        (dict(k=129), dict(group=1)),
+        (dict(n=-1), dict()),
+        (dict(dtype=7), dict()),
+    ]
+    for mkw, pkw in bad:
+        kw = dict(group=128, n_clusters=16, iters=20, seed=0)
+        kw.update(pkw)
+        st, _ = _ws_bytes(L, _mat(**mkw), any4.params(**kw))
+        assert st == 1, (mkw, pkw)
+    pr = any4.params(128, 16, 20, 0)
+    pr.reserved = 1
+    assert _ws_bytes(L, _mat(), pr)[0] == 1
+    # too long for register residency
+    assert _ws_bytes(L, _mat(k=65536), p)[0] == 2
+    # missing product pointer
+    m = _mat()
+    m.lut = None
+    assert _ws_bytes(L, m, p)[0] == 1
+    # zero rows need no pointers
+    m0 = any4.Any4Matrix()
+    m0.n_rows, m0.n_cols, m0.w_dtype = 0, 256, 1
+    assert _ws_bytes(L, m0, p)[0] == 0
+
+
+def test_quantize_rejects_before_launch(L):
+    """Errors are returned synchronously, before any HIP call."""
+    p = any4.params(128, 16, 20, 0)
+    m = _mat()
+    # no workspace
+    assert L.any4_quantize(ctypes.byref(m), 1, ctypes.byref(p), None, 0, None) == 3
+    assert L.any4_quantize(ctypes.byref(m), 1, ctypes.byref(p), 0x7000, 8, None) == 3
+    # invalid params win over the workspace check
+    assert L.any4_quantize(ctypes.byref(m), 1, ctypes.byref(any4.params(100)), None, 0, None) == 1
+    assert L.any4_quantize(None, 1, ctypes.byref(p), 0x7000, 256, None) == 1
+    assert L.any4_quantize(ctypes.byref(m), 1, None, 0x7000, 256, None) == 1
+    assert L.any4_quantize(ctypes.byref(m), -1, ctypes.byref(p), 0x7000, 256, None) == 1
+    # stage entry points validate too
+    assert L.any4_stage_seed(ctypes.byref(m), ctypes.byref(p), None, None, None) == 1
+    assert L.any4_stage_lloyd_step(ctypes.byref(_mat(k=500)), ctypes.byref(p), 1, 1, 1, None, None) == 1
+    assert L.any4_stage_full(ctypes.byref(m), ctypes.byref(p), None, None, None, 0, None) == 3
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert any4.status_string(s)
+    assert any4.status_string(0) == "ok"
+    assert "unknown" in any4.status_string(99)
+
+
+def test_no_gpu_fails_loudly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    w = torch.zeros((2, 256), dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError):
+        any4.quantize(w, torch.ones(256))

@@ -1,0 +1,307 @@
+"""Python binding of the MI355X any4 quantizer (libany4.so).
+
+Argument marshalling only: every step of the quantizer runs in the gfx950 kernels
+behind the C ABI declared in include/any4.h.  PyTorch supplies device memory and the
+current HIP stream.  There is no CPU fallback: without the built library, or
+without a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libany4.so")
+
+ANY4_F32, ANY4_BF16 = 0, 1
+ANY4_OK = 0
+ANY4_ERR_NONFINITE = 5
+WORKSPACE_BYTES = 256
+
+EXPORTED = [
+    "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
+    "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
+    "any4_stage_full",
+]
+
+
+class Any4Matrix(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("w_dtype", ctypes.c_int32),
+        ("matrix_index", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("n_cols", ctypes.c_int64),
+        ("act_absmean", ctypes.c_void_p),
+        ("row_offset", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("lut", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("offset", ctypes.c_void_p),
+        ("objective", ctypes.c_void_p),
+    ]
+
+
+class Any4Params(ctypes.Structure):
+    _fields_ = [
+        ("group", ctypes.c_int32),
+        ("n_clusters", ctypes.c_int32),
+        ("iters", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+class Any4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libany4.so (built in-tree by build.py / __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m weight_only_bit_row_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, MP, PP = ctypes.c_void_p, ctypes.POINTER(Any4Matrix), ctypes.POINTER(Any4Params)
+        L.any4_workspace_bytes.argtypes = [MP, ctypes.c_int32, PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.any4_quantize.argtypes = [MP, ctypes.c_int32, PP, P, ctypes.c_size_t, P]
+        L.any4_read_device_status.argtypes = [P, P]
+        L.any4_status_string.argtypes = [ctypes.c_int]
+        L.any4_status_string.restype = ctypes.c_char_p
+        L.any4_stage_scale.argtypes = [MP, PP, P, P, P, P, P]
+        L.any4_stage_seed.argtypes = [MP, PP, P, P, P]
+        L.any4_stage_lloyd_step.argtypes = [MP, PP, P, P, P, P, P]
+        L.any4_stage_pack.argtypes = [MP, PP, P, P, P, P, P]
+        L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
+        for name in EXPORTED:
+            if name != "any4_status_string":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().any4_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != ANY4_OK:
+        raise Any4Error(status, what)
+
+
+# ---------------------------------------------------------------------------------
+# torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_gpu(t):
+    torch = _torch()
+    if not torch.cuda.is_available():
+        raise RuntimeError("the any4 quantizer needs a ROCm GPU; none is visible")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+
+
+def _dtype_code(w) -> Tuple[int, object]:
+    torch = _torch()
+    if w.dtype == torch.bfloat16:
+        return ANY4_BF16, w
+    if w.dtype == torch.float32:
+        return ANY4_F32, w
+    if w.dtype in (torch.int16, torch.uint16):   # raw bf16 bits
+        return ANY4_BF16, w
+    raise TypeError(f"W must be float32 or bfloat16, got {w.dtype}")
+
+
+def params(group: int = 128, n_clusters: int = 16, iters: int = 20, seed: int = 0) -> Any4Params:
+    return Any4Params(group, n_clusters, iters, 0, seed)
+
+
+@dataclass
+class Quantized:
+    codes: object      # uint8 [N, K/2]
+    lut: object        # fp16 [N, n_clusters]
+    scale: object      # fp16 [N, K/group]
+    offset: object     # fp16 [N, K/group]
+    objective: object  # fp64 [N] or None
+
+
+def _alloc_outputs(n, k_cols, group, n_clusters, device, with_objective):
+    torch = _torch()
+    return Quantized(
+        codes=torch.empty((n, k_cols // 2), dtype=torch.uint8, device=device),
+        lut=torch.empty((n, n_clusters), dtype=torch.float16, device=device),
+        scale=torch.empty((n, k_cols // group), dtype=torch.float16, device=device),
+        offset=torch.empty((n, k_cols // group), dtype=torch.float16, device=device),
+        objective=(torch.empty((n,), dtype=torch.float64, device=device) if with_objective else None),
+    )
+
+
+def _matrix(w, act, out: Optional[Quantized], row_offset=0, matrix_index=0) -> Any4Matrix:
+    code, w = _dtype_code(w)
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("W must be a contiguous [N, K] tensor")
+    if act.dim() != 1 or not act.is_contiguous() or act.dtype != _torch().float32:
+        raise ValueError("act_absmean must be a contiguous float32 [K] tensor")
+    m = Any4Matrix()
+    m.w = _ptr(w)
+    m.w_dtype = code
+    m.matrix_index = matrix_index
+    m.n_rows, m.n_cols = int(w.shape[0]), int(w.shape[1])
+    m.act_absmean = _ptr(act)
+    m.row_offset = row_offset
+    if out is not None:
+        m.codes, m.lut = _ptr(out.codes), _ptr(out.lut)
+        m.scale, m.offset = _ptr(out.scale), _ptr(out.offset)
+        m.objective = _ptr(out.objective)
+    return m
+
+
+def workspace(device=None):
+    torch = _torch()
+    return torch.empty((WORKSPACE_BYTES,), dtype=torch.uint8, device=device or "cuda")
+
+
+def quantize_batch(items: Sequence[Tuple[object, object]], group: int = 128, n_clusters: int = 16,
+                   iters: int = 20, seed: int = 0, with_objective: bool = True,
+                   outputs: Optional[List[Quantized]] = None, ws=None,
+                   row_offsets: Optional[Sequence[int]] = None,
+                   matrix_indices: Optional[Sequence[int]] = None) -> List[Quantized]:
+    """Quantize several (W [N,K], act_absmean [K]) pairs in one call."""
+    if not items:
+        return []
+    w0 = items[0][0]
+    _require_gpu(w0)
+    device = w0.device
+    p = params(group, n_clusters, iters, seed)
+    if outputs is None:
+        outputs = [_alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, device, with_objective)
+                   for w, _ in items]
+    mats = (Any4Matrix * len(items))()
+    for i, (w, act) in enumerate(items):
+        mats[i] = _matrix(w, act, outputs[i],
+                          row_offset=(row_offsets[i] if row_offsets else 0),
+                          matrix_index=(matrix_indices[i] if matrix_indices else i))
+    if ws is None:
+        ws = workspace(device)
+    _check(lib().any4_quantize(mats, len(items), ctypes.byref(p), _ptr(ws), ws.numel(),
+                               _stream(device)), "any4_quantize")
+    return outputs
+
+
+def quantize(w, act, group: int = 128, n_clusters: int = 16, iters: int = 20, seed: int = 0,
+             row_offset: int = 0, matrix_index: int = 0, with_objective: bool = True,
+             out: Optional[Quantized] = None, ws=None) -> Quantized:
+    """Quantize one matrix W [N,K] (bf16/fp32) with E|x| act [K] (fp32)."""
+    _require_gpu(w)
+    p = params(group, n_clusters, iters, seed)
+    if out is None:
+        out = _alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, w.device, with_objective)
+    m = _matrix(w, act, out, row_offset, matrix_index)
+    if ws is None:
+        ws = workspace(w.device)
+    _check(lib().any4_quantize(ctypes.byref(m), 1, ctypes.byref(p), _ptr(ws), ws.numel(),
+                               _stream(w.device)), "any4_quantize")
+    return out
+
+
+def read_status(ws) -> int:
+    return lib().any4_read_device_status(_ptr(ws), _stream(ws.device))
+
+
+# ---------------------------------------------------------------------------------
+# stage entry points (parity tests)
+
+def stage_scale(w, act, group=128, n_clusters=16, row_offset=0, matrix_index=0):
+    torch = _torch()
+    _require_gpu(w)
+    N, K = w.shape
+    dev = w.device
+    ws_ = torch.empty((N, K), dtype=torch.float32, device=dev)
+    al = torch.empty((N, K // group), dtype=torch.float32, device=dev)
+    be = torch.empty((N, K // group), dtype=torch.float32, device=dev)
+    a = torch.empty((N, K), dtype=torch.float32, device=dev)
+    m = _matrix(w, act, None, row_offset, matrix_index)
+    p = params(group, n_clusters, 0, 0)
+    _check(lib().any4_stage_scale(ctypes.byref(m), ctypes.byref(p), _ptr(ws_), _ptr(al), _ptr(be),
+                                  _ptr(a), _stream(dev)), "any4_stage_scale")
+    return ws_, al, be, a
+
+
+def stage_seed(w, act, group=128, n_clusters=16, seed=0, row_offset=0, matrix_index=0):
+    torch = _torch()
+    _require_gpu(w)
+    N = w.shape[0]
+    c0 = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
+    picks = torch.empty((N, n_clusters), dtype=torch.int32, device=w.device)
+    m = _matrix(w, act, None, row_offset, matrix_index)
+    p = params(group, n_clusters, 0, seed)
+    _check(lib().any4_stage_seed(ctypes.byref(m), ctypes.byref(p), _ptr(c0), _ptr(picks),
+                                 _stream(w.device)), "any4_stage_seed")
+    return c0, picks
+
+
+def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16):
+    torch = _torch()
+    _require_gpu(w)
+    N, K = w.shape
+    assign = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    c_out = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
+    obj = torch.empty((N,), dtype=torch.float64, device=w.device)
+    m = _matrix(w, act, None)
+    p = params(group, n_clusters, 1, 0)
+    c_in = c_in.contiguous().to(torch.float32)
+    _check(lib().any4_stage_lloyd_step(ctypes.byref(m), ctypes.byref(p), _ptr(c_in), _ptr(assign),
+                                       _ptr(c_out), _ptr(obj), _stream(w.device)),
+           "any4_stage_lloyd_step")
+    return assign, c_out, obj
+
+
+def stage_pack(n_rows, n_cols, assign, c, alpha, beta, group=128, n_clusters=16):
+    _require_gpu(assign)
+    out = _alloc_outputs(n_rows, n_cols, group, n_clusters, assign.device, False)
+    m = Any4Matrix()
+    m.n_rows, m.n_cols = n_rows, n_cols
+    m.w_dtype = ANY4_F32
+    m.w, m.act_absmean = _ptr(assign), _ptr(c)   # not read by the pack stage
+    m.codes, m.lut, m.scale, m.offset = _ptr(out.codes), _ptr(out.lut), _ptr(out.scale), _ptr(out.offset)
+    p = params(group, n_clusters, 0, 0)
+    _check(lib().any4_stage_pack(ctypes.byref(m), ctypes.byref(p), _ptr(assign), _ptr(c),
+                                 _ptr(alpha), _ptr(beta), _stream(assign.device)), "any4_stage_pack")
+    return out
+
+
+def stage_full(w, act, group=128, n_clusters=16, iters=20, seed=0, row_offset=0, matrix_index=0):
+    """Full path for one matrix plus the fp32 final centroids and the k-means++ picks."""
+    torch = _torch()
+    _require_gpu(w)
+    N = w.shape[0]
+    out = _alloc_outputs(N, w.shape[1], group, n_clusters, w.device, True)
+    c_final = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
+    picks = torch.empty((N, n_clusters), dtype=torch.int32, device=w.device)
+    m = _matrix(w, act, out, row_offset, matrix_index)
+    p = params(group, n_clusters, iters, seed)
+    ws = workspace(w.device)
+    _check(lib().any4_stage_full(ctypes.byref(m), ctypes.byref(p), _ptr(c_final), _ptr(picks),
+                                 _ptr(ws), ws.numel(), _stream(w.device)), "any4_stage_full")
+    return out, c_final, picks, ws

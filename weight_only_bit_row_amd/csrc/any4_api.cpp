@@ -1,0 +1,243 @@
+// C ABI of the any4 quantizer (declared in include/any4.h): argument validation,
+// batching of matrices into row-kernel launches, and the stage entry points.
+// Everything here runs on the host and only enqueues work on the caller's stream.
+#include "any4.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "any4_launch.h"
+
+namespace {
+
+using any4::LaunchArgs;
+using any4::MatDesc;
+using any4::RowConfig;
+
+constexpr size_t kWorkspaceBytes = 256;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_params(const any4_params* p) {
+  if (!p) return ANY4_ERR_INVALID_ARG;
+  if (p->group < 2 || !is_pow2(p->group)) return ANY4_ERR_INVALID_ARG;
+  if (!(p->n_clusters == 2 || p->n_clusters == 4 || p->n_clusters == 8 || p->n_clusters == 16))
+    return ANY4_ERR_INVALID_ARG;
+  if (p->iters < 0 || p->reserved != 0) return ANY4_ERR_INVALID_ARG;
+  return ANY4_OK;
+}
+
+int check_matrix(const any4_matrix* m, const any4_params* p, bool need_products) {
+  if (!m) return ANY4_ERR_INVALID_ARG;
+  if (m->n_rows < 0 || m->n_cols < 2 || (m->n_cols & 1)) return ANY4_ERR_INVALID_ARG;
+  if (m->n_cols % p->group != 0) return ANY4_ERR_INVALID_ARG;
+  if (m->w_dtype != ANY4_F32 && m->w_dtype != ANY4_BF16) return ANY4_ERR_INVALID_ARG;
+  if (m->row_offset < 0 || m->row_offset > INT64_MAX - m->n_rows) return ANY4_ERR_INVALID_ARG;
+  if (m->n_cols > any4::kMaxCols) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows == 0) return ANY4_OK;
+  if (!m->w || !m->act_absmean) return ANY4_ERR_INVALID_ARG;
+  if (need_products && (!m->codes || !m->lut || !m->scale || !m->offset))
+    return ANY4_ERR_INVALID_ARG;
+  return ANY4_OK;
+}
+
+MatDesc make_desc(const any4_matrix* m) {
+  MatDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.w = m->w;
+  d.act = m->act_absmean;
+  d.n_rows = m->n_rows;
+  d.n_cols = m->n_cols;
+  d.row_offset = m->row_offset;
+  d.dtype = m->w_dtype;
+  d.matrix_index = m->matrix_index;
+  d.codes = m->codes;
+  d.lut = m->lut;
+  d.scale = m->scale;
+  d.offset = m->offset;
+  d.objective = m->objective;
+  return d;
+}
+
+LaunchArgs make_args(const any4_params* p, int nw, uint32_t* status) {
+  LaunchArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.group = p->group;
+  a.n_clusters = p->n_clusters;
+  a.iters = p->iters;
+  a.nw = nw;
+  a.seed = p->seed;
+  a.status = status;
+  return a;
+}
+
+int launch_one(const LaunchArgs& base, const MatDesc& d, int mode, hipStream_t stream) {
+  if (d.n_rows == 0) return ANY4_OK;
+  const RowConfig cfg = any4::choose_config(d.n_cols);
+  LaunchArgs a = base;
+  a.nw = cfg.nw;
+  a.m[0] = d;
+  a.n_mats = 1;
+  a.row_start[0] = 0;
+  for (int i = 1; i <= any4::kMaxMats; ++i) a.row_start[i] = d.n_rows;
+  const hipError_t e = any4::launch_rows(a, cfg, mode, d.n_rows, stream);
+  return e == hipSuccess ? ANY4_OK : ANY4_ERR_HIP;
+}
+
+int validate_batch(const any4_matrix* mats, int32_t count, const any4_params* p) {
+  int st = check_params(p);
+  if (st != ANY4_OK) return st;
+  if (count < 0 || (count > 0 && !mats)) return ANY4_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i) {
+    st = check_matrix(&mats[i], p, true);
+    if (st != ANY4_OK) return st;
+  }
+  return ANY4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* any4_status_string(int status) {
+  switch (status) {
+    case ANY4_OK: return "ok";
+    case ANY4_ERR_INVALID_ARG: return "invalid argument";
+    case ANY4_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case ANY4_ERR_WORKSPACE: return "workspace missing or too small";
+    case ANY4_ERR_HIP: return "HIP launch or runtime error";
+    case ANY4_ERR_NONFINITE: return "a row held a non-finite or out-of-range value";
+    default: return "unknown status";
+  }
+}
+
+int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_params* params,
+                         size_t* bytes_out) {
+  if (!bytes_out) return ANY4_ERR_INVALID_ARG;
+  const int st = validate_batch(mats, count, params);
+  if (st != ANY4_OK) return st;
+  *bytes_out = kWorkspaceBytes;
+  return ANY4_OK;
+}
+
+int any4_quantize(const any4_matrix* mats, int32_t count, const any4_params* params,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate_batch(mats, count, params);
+  if (st != ANY4_OK) return st;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return ANY4_ERR_WORKSPACE;
+  uint32_t* status = static_cast<uint32_t*>(workspace);
+  if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
+
+  // Matrices sharing a row geometry go into one launch (up to kMaxMats each);
+  // longer rows first so that the longest blocks start earliest.
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < count; ++i)
+    if (mats[i].n_rows > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return mats[x].n_cols > mats[y].n_cols;
+  });
+  size_t i = 0;
+  while (i < order.size()) {
+    const RowConfig cfg = any4::choose_config(mats[order[i]].n_cols);
+    LaunchArgs a = make_args(params, cfg.nw, status);
+    int64_t rows = 0;
+    a.n_mats = 0;
+    while (i < order.size() && a.n_mats < any4::kMaxMats) {
+      const RowConfig c2 = any4::choose_config(mats[order[i]].n_cols);
+      if (c2.e != cfg.e || c2.nw != cfg.nw) break;
+      if (rows + mats[order[i]].n_rows > INT32_MAX) break;
+      a.row_start[a.n_mats] = rows;
+      a.m[a.n_mats] = make_desc(&mats[order[i]]);
+      rows += mats[order[i]].n_rows;
+      ++a.n_mats;
+      ++i;
+    }
+    for (int j = a.n_mats; j <= any4::kMaxMats; ++j) a.row_start[j] = rows;
+    if (any4::launch_rows(a, cfg, any4::MODE_FULL, rows, stream) != hipSuccess)
+      return ANY4_ERR_HIP;
+  }
+  return ANY4_OK;
+}
+
+int any4_read_device_status(const void* workspace, hipStream_t stream) {
+  if (!workspace) return ANY4_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return ANY4_ERR_HIP;
+  uint32_t st = 0;
+  if (hipMemcpy(&st, workspace, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
+    return ANY4_ERR_HIP;
+  return st == 0 ? ANY4_OK : static_cast<int>(st);
+}
+
+int any4_stage_scale(const any4_matrix* m, const any4_params* params, float* w_s, float* alpha,
+                     float* beta, float* a, hipStream_t stream) {
+  int st = check_params(params);
+  if (st == ANY4_OK) st = check_matrix(m, params, false);
+  if (st != ANY4_OK) return st;
+  if (m->n_rows > 0 && (!w_s || !alpha || !beta || !a)) return ANY4_ERR_INVALID_ARG;
+  MatDesc d = make_desc(m);
+  d.ws_out = w_s;
+  d.alpha_out = alpha;
+  d.beta_out = beta;
+  d.a_out = a;
+  return launch_one(make_args(params, 1, nullptr), d, any4::MODE_SCALE, stream);
+}
+
+int any4_stage_seed(const any4_matrix* m, const any4_params* params, float* c0, int32_t* picks,
+                    hipStream_t stream) {
+  int st = check_params(params);
+  if (st == ANY4_OK) st = check_matrix(m, params, false);
+  if (st != ANY4_OK) return st;
+  if (m->n_rows > 0 && (!c0 || !picks)) return ANY4_ERR_INVALID_ARG;
+  MatDesc d = make_desc(m);
+  d.c_out = c0;
+  d.picks_out = picks;
+  return launch_one(make_args(params, 1, nullptr), d, any4::MODE_SEED, stream);
+}
+
+int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const float* c_in,
+                          uint8_t* assign, float* c_out, double* objective, hipStream_t stream) {
+  int st = check_params(params);
+  if (st == ANY4_OK) st = check_matrix(m, params, false);
+  if (st != ANY4_OK) return st;
+  if (m->n_rows > 0 && (!c_in || !assign || !c_out)) return ANY4_ERR_INVALID_ARG;
+  MatDesc d = make_desc(m);
+  d.c_in = c_in;
+  d.assign_out = assign;
+  d.c_out = c_out;
+  d.objective = objective;
+  return launch_one(make_args(params, 1, nullptr), d, any4::MODE_STEP, stream);
+}
+
+int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8_t* assign,
+                    const float* c, const float* alpha, const float* beta, hipStream_t stream) {
+  int st = check_params(params);
+  if (st == ANY4_OK) st = check_matrix(m, params, false);
+  if (st != ANY4_OK) return st;
+  if (m->n_rows == 0) return ANY4_OK;
+  if (!m->codes || !m->lut || !m->scale || !m->offset || !assign || !c || !alpha || !beta)
+    return ANY4_ERR_INVALID_ARG;
+  const MatDesc d = make_desc(m);
+  return any4::launch_pack(d, params->group, params->n_clusters, assign, c, alpha, beta,
+                           stream) == hipSuccess
+             ? ANY4_OK
+             : ANY4_ERR_HIP;
+}
+
+int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_final,
+                    int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate_batch(m, 1, params);
+  if (st != ANY4_OK) return st;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return ANY4_ERR_WORKSPACE;
+  uint32_t* status = static_cast<uint32_t*>(workspace);
+  if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
+  MatDesc d = make_desc(m);
+  d.c_out = c_final;
+  d.picks_out = picks;
+  return launch_one(make_args(params, 1, status), d, any4::MODE_FULL, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI layer (any4_api.cpp) and the gfx950 kernels
+// (any4_kernels.hip).  Not installed; the public interface is include/any4.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace any4 {
+
+constexpr int kMaxMats = 8;       // matrices per launch (descriptors travel as kernel arguments)
+constexpr int kMaxClusters = 16;
+constexpr int kMaxCols = 32768;   // 8 waves x 64 lanes x 64 elements held in registers
+
+enum Mode : int { MODE_FULL = 0, MODE_SCALE = 1, MODE_SEED = 2, MODE_STEP = 3 };
+
+struct MatDesc {
+  const void* w;
+  const float* act;
+  int64_t n_rows;
+  int64_t n_cols;
+  int64_t row_offset;
+  int32_t dtype;
+  int32_t matrix_index;
+  // products
+  uint8_t* codes;
+  uint16_t* lut;
+  uint16_t* scale;
+  uint16_t* offset;
+  double* objective;
+  // stage inputs / outputs (NULL unless a stage entry point sets them)
+  float* ws_out;
+  float* alpha_out;
+  float* beta_out;
+  float* a_out;
+  const float* c_in;
+  float* c_out;
+  uint8_t* assign_out;
+  int32_t* picks_out;
+};
+
+struct LaunchArgs {
+  MatDesc m[kMaxMats];
+  int64_t row_start[kMaxMats + 1];  // block b belongs to matrix i when row_start[i] <= b < row_start[i+1]
+  int32_t n_mats;
+  int32_t group;
+  int32_t n_clusters;
+  int32_t iters;
+  int32_t nw;                       // waves per row (one workgroup per row)
+  int32_t pad_;
+  uint64_t seed;
+  uint32_t* status;                 // device status word or NULL
+};
+
+// Row-kernel launch geometry for a row length: elements per lane E and waves per row.
+struct RowConfig {
+  int e;
+  int nw;
+};
+RowConfig choose_config(int64_t n_cols);
+
+// Launch one row kernel over all rows of args (args.nw must match cfg.nw).
+hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t n_blocks,
+                       hipStream_t stream);
+// Clear the status word (a one-thread kernel: no memset node is recorded).
+hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
+// Emission-only kernel behind any4_stage_pack.
+hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_t* assign,
+                       const float* c, const float* alpha, const float* beta, hipStream_t stream);
+
+}  // namespace any4
