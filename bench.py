@@ -1,0 +1,217 @@
+"""Throughput of the any4 quantizer on one MI355X.
+
+A step is one any4_quantize call over a whole synthetic Llama3-8B-like up_proj weight
+(14336 x 4096 bf16, group 128, 16 clusters, 20 Lloyd rounds): scaling, k-means++,
+Lloyd, final assignment and emission.  Inputs are resident in HBM before timing;
+outputs are preallocated.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --profile-steps 3          # short run for rocprofv3
+  python bench.py --copy-calibration         # plain copy of known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+KERNEL_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "any4_rows_up_proj_counters.md")
+
+PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed FMA counted as 2 flops x 2 lanes)
+METRIC = "Lloyd elem-iters/sec and % FP32 VALU peak; ms per 14336x4096 matrix"
+
+
+def credited_flops_per_element(k: int, iters: int) -> int:
+    """Algorithmic work per weight element for the whole call: scaling (~6 flop),
+    k-means++ (4 per centre), `iters` Lloyd rounds of 3k+1 (k subtractions, k squares,
+    k-1 compares, 2 adds) and a final E-step plus objective (3k+2)."""
+    return 6 + 4 * k + iters * (3 * k + 1) + (3 * k + 2)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(m, group, k, iters, n_rows_sample=14336):
+    """The CPU oracle, as it is, on a bounded row sample of the same matrix, spread over
+    the host's cores with threads (ctypes releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    rows = min(n_rows_sample, m.w.shape[0])
+    bounds = np.linspace(0, rows, cores + 1).astype(int)
+
+    def work(c):
+        lo, hi = bounds[c], bounds[c + 1]
+        if hi > lo:
+            oracle.quantize(m.w[lo:hi], m.dtype, m.act, group, k, iters, seed=0, row_offset=int(lo))
+
+    oracle.lib()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(work, range(cores)))
+    dt = time.perf_counter() - t0
+    K = m.w.shape[1]
+    return {
+        "value": rows * K * iters / dt,
+        "unit": "elem-iters/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"first {rows} of {m.w.shape[0]} rows of the same matrix, full path "
+                  f"(scale, k-means++, {iters} Lloyd rounds, final E-step, emission); "
+                  f"{dt:.2f} s wall on {cores} threads",
+    }
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many quantize calls (for rocprofv3), no baseline")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the quantizer's rows are independent and this "
+              "build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import weight_only_bit_row_amd as any4
+    from workloads import make
+
+    wl = make("up_proj")
+    m = wl.matrices[0]
+    N, K = m.w.shape
+    g, k, iters = wl.group, wl.n_clusters, wl.iters
+    dev = torch.device("cuda:0")
+    w = torch.from_numpy(m.w.view(np.int16)).to(dev).view(torch.bfloat16)
+    act = torch.from_numpy(m.act).to(dev)
+    out = any4.quantize(w, act, group=g, n_clusters=k, iters=iters)   # allocates outputs
+    ws = any4.workspace(dev)
+    torch.cuda.synchronize()
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            any4.quantize(w, act, group=g, n_clusters=k, iters=iters, out=out, ws=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "status": any4.read_status(ws)}))
+        return
+
+    stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
+
+    def timed(n_iters, steps, warmup):
+        for _ in range(warmup):
+            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(stream)
+            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        return wall, ms
+
+    wall, ms = timed(iters, args.steps, args.warmup)
+    status = any4.read_status(ws)
+    _, ms0 = timed(0, max(5, args.steps // 2), 2)
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = float(np.mean(ms))
+    t20, t0_ = float(np.median(ms)), float(np.median(ms0))
+    elem_iters = N * K * iters
+    flops = credited_flops_per_element(k, iters) * N * K
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    traffic = load_traffic()
+
+    line = {
+        "metric": METRIC,
+        "value": elem_iters / (ms_step * 1e-3),
+        "unit": "elem-iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Llama3-8B-like up_proj 14336x4096 bf16, group 128, 16 clusters, "
+                               "20 Lloyd rounds, Philox seed 0",
+                   "n_rows": N, "n_cols": K, "group": g, "n_clusters": k, "iters": iters},
+        "ms_per_matrix": t20,
+        "lloyd_ms": t20 - t0_,
+        "lloyd_elem_iters_per_s": elem_iters / ((t20 - t0_) * 1e-3) if t20 > t0_ else None,
+        "lloyd_pct_fp32_peak_credited": (elem_iters * (3 * k + 1) / ((t20 - t0_) * 1e-3) / 1e12
+                                         / PEAK_FP32_TFLOPS * 100) if t20 > t0_ else None,
+        "ms_iters0": t0_,
+        "device_status": status,
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS,
+            "traffic": traffic,
+            "kernel": "any4_rows_kernel<E=%d, waves/row=%d>" % any4.launch_geometry(K),
+            "credited_flops_per_element": credited_flops_per_element(k, iters),
+            "kernel_ms_mean_hip_events": ms_kernel,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(m, g, k, iters)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

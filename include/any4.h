@@ -114,6 +114,12 @@ int any4_read_device_status(const void* workspace, hipStream_t stream);
 /* Static English text for a status code. */
 const char* any4_status_string(int status);
 
+/* Launch geometry the library uses for rows of n_cols columns: each row is one
+ * workgroup of *waves_per_row wave64s, each lane holding *elems_per_lane
+ * consecutive columns.  Host-only; returns ANY4_ERR_INVALID_ARG for bad pointers
+ * or n_cols outside [2, 32768]. */
+int any4_launch_geometry(int64_t n_cols, int32_t* elems_per_lane, int32_t* waves_per_row);
+
 /* ---- stage entry points: the same device code as any4_quantize, stopped after
  * one step, for parity tests against the CPU oracle.  One matrix each; the
  * any4_matrix output fields that a stage does not produce are ignored. ---- */

@@ -123,6 +123,18 @@ def test_quantize_rejects_before_launch(L):
     assert L.any4_stage_full(ctypes.byref(m), ctypes.byref(p), None, None, None, 0, None) == 3
 
 
+def test_launch_geometry(L):
+    assert any4.launch_geometry(4096) == (32, 2)
+    assert any4.launch_geometry(512) == (8, 1)
+    e, nw = any4.launch_geometry(28672)
+    assert e * nw * 64 >= 28672 and nw <= 8
+    for k in [2, 100, 1000, 2048, 14336, 32768]:
+        e, nw = any4.launch_geometry(k)
+        assert e * nw * 64 >= k
+    with pytest.raises(any4.Any4Error):
+        any4.launch_geometry(65536)
+
+
 def test_status_strings(L):
     for s in range(6):
         assert any4.status_string(s)

@@ -22,6 +22,7 @@ WORKSPACE_BYTES = 256
 
 EXPORTED = [
     "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
+    "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
     "any4_stage_full",
 ]
@@ -81,11 +82,20 @@ def lib():
         L.any4_stage_lloyd_step.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_pack.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
+        L.any4_launch_geometry.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int32)]
         for name in EXPORTED:
             if name != "any4_status_string":
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def launch_geometry(n_cols: int) -> Tuple[int, int]:
+    """(elements per lane, waves per row) of the row kernel for this row length."""
+    e, nw = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().any4_launch_geometry(n_cols, ctypes.byref(e), ctypes.byref(nw)), "any4_launch_geometry")
+    return e.value, nw.value
 
 
 def status_string(status: int) -> str:

@@ -115,6 +115,15 @@ const char* any4_status_string(int status) {
   }
 }
 
+int any4_launch_geometry(int64_t n_cols, int32_t* elems_per_lane, int32_t* waves_per_row) {
+  if (!elems_per_lane || !waves_per_row || n_cols < 2 || n_cols > any4::kMaxCols)
+    return ANY4_ERR_INVALID_ARG;
+  const RowConfig cfg = any4::choose_config(n_cols);
+  *elems_per_lane = cfg.e;
+  *waves_per_row = cfg.nw;
+  return ANY4_OK;
+}
+
 int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_params* params,
                          size_t* bytes_out) {
   if (!bytes_out) return ANY4_ERR_INVALID_ARG;

@@ -16,9 +16,13 @@
 //              Philox4x32-10 draw per (row, step)
 //   Lloyd      per round: sort the <=16 centroids, merge equal values (lowest draw
 //              index kept), compute the exact fp32 switch point between each pair of
-//              sorted neighbours, then each element finds its cluster by a 4-level
-//              binary search over the switch points (LDS, conflict-free: 15 entries),
-//              and adds (a_j, a_j*w_S_j) in fp64 (the product is exact) into
+//              sorted neighbours, and tabulate them over fixed 1/16-wide cells of the
+//              scaled range (per cell: cluster position at the cell start and the <= 2
+//              switch points inside it).  Each element's cell is fixed for the whole
+//              row, so its E-step is one LDS table read and two compares; a round
+//              whose table would need a third switch point in one cell uses a 4-level
+//              binary search over all switch points instead (same result).  The
+//              element then adds (a_j, a_j*w_S_j) in fp64 (the product is exact) into
 //              lane-private LDS bins; bins are reduced per wave in a fixed order
 //              (no global atomics)
 //   emit       final assignment, nibble packing, fp16 LUT/scale/offset, fp64 objective
@@ -65,7 +69,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 // Shared memory: a fixed header, then per-wave lane-private bins [nw][2][16][64] fp64.
 struct Smem {
   float c[kMaxClusters];      // centroids in draw order
-  float thr[kMaxClusters];    // switch points between sorted neighbours, +inf padded
+  float thr[kMaxClusters + 4];       // switch points between sorted neighbours, +inf padded
+  uint32_t tcell[kMaxClusters + 4];  // cell of each switch point, kMaxCells beyond the last
   float sv[kMaxClusters];     // sorted distinct centroid values
   int sidx[kMaxClusters];     // lowest draw index holding each sorted value
   double red[2 * kMaxClusters];         // reduced bins: S0[16], S1[16]
@@ -87,7 +92,19 @@ struct Smem {
 };
 
 constexpr size_t kSmemHdr = (sizeof(Smem) + 15) & ~size_t(15);
-constexpr size_t kBinBytesPerWave = 2 * kMaxClusters * kWave * sizeof(double);  // 16 KiB
+constexpr int kCellsPerUnit = 16;                          // cell width 1/16 of a scaled unit
+constexpr int kMaxCells = kCellsPerUnit * kMaxClusters;    // cells cover [0, n_clusters)
+constexpr size_t kTableBytes = kMaxCells * 16;             // {T1, T2, position, -} per cell
+// Lane-private fp64 bins, optionally shared by the lanes l, l + 64/kBinShare, ... of a
+// wave.  Sharers sit in different 16-lane groups of an LDS instruction, so they never
+// collide on a bank within a cycle, and the instruction's fixed lane-group order keeps
+// the accumulation order (and the fp64 result) deterministic.
+#ifndef ANY4_BIN_SHARE
+#define ANY4_BIN_SHARE 2
+#endif
+constexpr int kBinShare = ANY4_BIN_SHARE;
+constexpr int kBinCols = kWave / kBinShare;
+constexpr size_t kBinBytesPerWave = 2 * kMaxClusters * kBinCols * sizeof(double);
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -107,35 +124,83 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Wave-level reductions and scans with DPP lane moves (VALU latency, no LDS round
+// trip).  Controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror
+// 0x141, row_mirror 0x140, row_shr:n 0x110+n, row_bcast:15 0x142, row_bcast:31 0x143.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(dpp<CTRL, ROW_MASK>(__float_as_int(v)));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp<CTRL, ROW_MASK>(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(dpp<CTRL, ROW_MASK>(static_cast<int>(v >> 32)));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dppd(double v) {
+  return __longlong_as_double(
+      static_cast<long long>(dpp64<CTRL, ROW_MASK>(static_cast<unsigned long long>(__double_as_longlong(v)))));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// max/min of the wave, uniform result
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
-  return v;
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));  // every lane of a row now holds the row's max
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v = fminf(v, __shfl_xor(v, s));
-  return v;
+  v = fminf(v, dppf<0xB1>(v));
+  v = fminf(v, dppf<0x4E>(v));
+  v = fminf(v, dppf<0x141>(v));
+  v = fminf(v, dppf<0x140>(v));
+  return fminf(fminf(readlane_f(v, 0), readlane_f(v, 16)), fminf(readlane_f(v, 32), readlane_f(v, 48)));
 }
+// fp64 sum of the wave in a fixed order, uniform result
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
+  v += dppd<0xB1>(v);
+  v += dppd<0x4E>(v);
+  v += dppd<0x141>(v);
+  v += dppd<0x140>(v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+// inclusive prefix sums over the wave's lanes
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  v += dpp64<0x111>(v);
+  v += dpp64<0x112>(v);
+  v += dpp64<0x114>(v);
+  v += dpp64<0x118>(v);
+  v += dpp64<0x142, 0xA>(v);
+  v += dpp64<0x143, 0xC>(v);
   return v;
 }
-__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
-#pragma unroll
-  for (int s = 1; s < kWave; s <<= 1) {
-    const unsigned long long t = __shfl_up(v, s);
-    if (lane >= s) v += t;
-  }
-  return v;
-}
-__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int s = 1; s < kWave; s <<= 1) {
-    const double t = __shfl_up(v, s);
-    if (lane >= s) v += t;
-  }
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  v += dppd<0x111>(v);
+  v += dppd<0x112>(v);
+  v += dppd<0x114>(v);
+  v += dppd<0x118>(v);
+  v += dppd<0x142, 0xA>(v);
+  v += dppd<0x143, 0xC>(v);
   return v;
 }
 
@@ -171,38 +236,87 @@ __device__ float switch_point(float cl, int il, float cr, int ir) {
   return __uint_as_float(hi);
 }
 
+// Fixed grid over the scaled range: cell h holds x in [h/16, (h+1)/16).  x * 16 is
+// exact, so the cell is monotone in x; values past the last cell clamp into it.
+__device__ __forceinline__ uint32_t cell_of(float x, int G) {
+  const uint32_t h = static_cast<uint32_t>(x * static_cast<float>(kCellsPerUnit));
+  return h < static_cast<uint32_t>(G) ? h : static_cast<uint32_t>(G - 1);
+}
+
 // Wave 0 only: from S.c (k values), build the sorted distinct values, their lowest
-// draw index, and the switch points S.thr[0..U-2] (+inf beyond).
-__device__ void build_structure(Smem& S, int k, int lane) {
+// draw index, the switch points S.thr[0..U-2] (+inf beyond) and their cells.  The
+// centroids are broadcast to uniform registers; each lane ranks its own centroid.
+__device__ void build_structure(Smem& S, int k, int G, int lane) {
   const float inf = __builtin_huge_valf();
   float ct = (lane < k) ? S.c[lane] : inf;
   if (ct == 0.0f) ct = 0.0f;  // -0 -> +0 so that bit patterns order like values
+  float cu[kMaxClusters];
+#pragma unroll
+  for (int u = 0; u < kMaxClusters; ++u) cu[u] = readlane_f(ct, u);
   bool first = lane < k;
-  for (int u = 0; u < k; ++u) {
-    float cu = S.c[u];
-    if (cu == 0.0f) cu = 0.0f;
-    if (u < lane && cu == ct) first = false;
-  }
+#pragma unroll
+  for (int u = 0; u < kMaxClusters; ++u)
+    if (u < lane && cu[u] == ct) first = false;
   const unsigned long long fm = __ballot(first);
   int less = 0;
-  for (int u = 0; u < k; ++u) {
-    float cu = S.c[u];
-    if (cu == 0.0f) cu = 0.0f;
-    if (((fm >> u) & 1ull) && cu < ct) ++less;
-  }
+#pragma unroll
+  for (int u = 0; u < kMaxClusters; ++u)
+    if (((fm >> u) & 1ull) && cu[u] < ct) ++less;
   const int U = __popcll(fm);
   if (first) {
     S.sv[less] = ct;
     S.sidx[less] = lane;
   }
   wave_lds_fence();
-  if (lane < kMaxClusters) {
+  if (lane < kMaxClusters + 4) {
     float t = inf;
-    if (lane + 1 < U) t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
+    uint32_t tc = kMaxCells;
+    if (lane + 1 < U) {
+      t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
+      tc = cell_of(t, G);
+    }
     S.thr[lane] = t;
+    S.tcell[lane] = tc;
   }
   if (lane == 0) S.n_unique = U;
   wave_lds_fence();
+}
+
+// All threads: the per-cell table for this round.  For cell h, `position` counts the
+// switch points in earlier cells (all below any x of cell h, by monotonicity of
+// cell_of), and T1 <= T2 are the switch points inside the cell (+inf if none), so the
+// cluster position of x is position + [x >= T1] + [x >= T2].  Returns true when a
+// cell holds a third switch point (the round then uses the binary search).
+__device__ __forceinline__ bool build_table(const Smem& S, unsigned char* table, int G, int tid,
+                                            int nthreads) {
+  constexpr int CPT = kMaxCells / kWave;  // cells per thread with one wave
+  const float inf = __builtin_huge_valf();
+  const uint32_t t7 = S.tcell[7];
+  uint32_t h[CPT];
+  int base[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    h[j] = static_cast<uint32_t>(tid + j * nthreads);
+    base[j] = (t7 < h[j]) ? 8 : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j] + 3] < h[j]) ? 4 : 0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j] + 1] < h[j]) ? 2 : 0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j]] < h[j]) ? 1 : 0;
+  bool over = false;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    if (h[j] < static_cast<uint32_t>(G)) {
+      const int b = base[j];
+      const float t1 = (S.tcell[b] == h[j]) ? S.thr[b] : inf;
+      const float t2 = (S.tcell[b + 1] == h[j]) ? S.thr[b + 1] : inf;
+      if (S.tcell[b + 2] == h[j]) over = true;
+      reinterpret_cast<float4*>(table)[h[j]] = make_float4(t1, t2, __uint_as_float(b), 0.0f);
+    }
+  }
+  return over;
 }
 
 // Cluster position (index into the sorted distinct values) of x: the number of
@@ -221,6 +335,7 @@ template <int E>
 __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, int col0,
                                          float (&x)[E], float (&act)[E]) {
   const bool full = col0 + E <= K;
+  const int nv = K - col0;  // valid columns of this lane (may be <= 0 or >= E)
   if (M.dtype == 1) {
     const uint16_t* src = static_cast<const uint16_t*>(M.w) + row * (int64_t)K + col0;
     if (full && (K & 7) == 0 && ((reinterpret_cast<uintptr_t>(M.w) & 15) == 0)) {
@@ -236,7 +351,7 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < E; ++m) x[m] = (col0 + m < K) ? bf16_bits_to_float(src[m]) : 0.0f;
+      for (int m = 0; m < E; ++m) x[m] = (m < nv) ? bf16_bits_to_float(src[m]) : 0.0f;
     }
   } else {
     const float* src = static_cast<const float*>(M.w) + row * (int64_t)K + col0;
@@ -251,7 +366,7 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < E; ++m) x[m] = (col0 + m < K) ? src[m] : 0.0f;
+      for (int m = 0; m < E; ++m) x[m] = (m < nv) ? src[m] : 0.0f;
     }
   }
   const float* asrc = M.act + col0;
@@ -266,7 +381,7 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < E; ++m) act[m] = (col0 + m < K) ? asrc[m] : 0.0f;
+    for (int m = 0; m < E; ++m) act[m] = (m < nv) ? asrc[m] : 0.0f;
   }
 }
 
@@ -280,6 +395,7 @@ __device__ __forceinline__ void finish_group(float mn, float mx, float qr, float
   const float beta = mn;
   if (!is_finite(alpha)) bad = true;
   for (int m = 0; m < n; ++m) {
+    asm volatile("" : "+v"(x[m]), "+v"(act[m]));  // one division in flight at a time
     float ws = 0.0f;
     if (alpha > 0.0f) {
       const float diff = x[m] - beta;
@@ -347,7 +463,12 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], float
   }
   const int L = g / E;
   if (L <= kWave) {
-    for (int s = 1; s < L; s <<= 1) {
+    // lanes of a group are aligned: combine pairs, quads, 8 and 16 with DPP moves
+    if (L >= 2) { mn = fminf(mn, dppf<0xB1>(mn)); mx = fmaxf(mx, dppf<0xB1>(mx)); }
+    if (L >= 4) { mn = fminf(mn, dppf<0x4E>(mn)); mx = fmaxf(mx, dppf<0x4E>(mx)); }
+    if (L >= 8) { mn = fminf(mn, dppf<0x141>(mn)); mx = fmaxf(mx, dppf<0x141>(mx)); }
+    if (L >= 16) { mn = fminf(mn, dppf<0x140>(mn)); mx = fmaxf(mx, dppf<0x140>(mx)); }
+    for (int s = 16; s < L; s <<= 1) {
       mn = fminf(mn, __shfl_xor(mn, s));
       mx = fmaxf(mx, __shfl_xor(mx, s));
     }
@@ -379,57 +500,106 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], float
 }
 
 // ---------------------------------------------------------------------------------
-// E-step + M-step over the lane's elements: position by binary search, then the two
-// Eq. 23 sums into lane-private fp64 bins (address pos*64 + lane: conflict-free).
+// One pass over the lane's elements with the current centroids.  The cluster
+// position comes from the cell table (TABLE) or the binary search; ACCUM adds the two
+// Eq. 23 sums into lane-private fp64 bins (address pos*64 + lane: conflict-free;
 // (double)a * (double)w_S is exact, so only the order of the fp64 additions differs
-// from a sequential sum.
-// The resident row is re-declared opaque on every round: otherwise the compiler
-// hoists the loop-invariant fp64 conversions out of the Lloyd loop and holds 4E
-// extra registers.
-template <int E>
-__device__ __forceinline__ void pin_row(float (&x)[E], float (&a)[E]) {
-#pragma unroll
-  for (int m = 0; m < E; ++m) asm volatile("" : "+v"(x[m]), "+v"(a[m]));
-}
+// from a sequential sum); STEP also stores the assignment and sums the objective;
+// FINAL packs the codes and sums the objective.
+enum PassKind { PASS_ACCUM = 0, PASS_STEP = 1, PASS_FINAL = 2 };
 
-template <int E>
-__device__ __forceinline__ void em_pass(float (&x)[E], float (&a)[E], const Smem& S,
-                                        double* bins, int lane) {
-  pin_row<E>(x, a);
+template <int E, int KIND, bool TABLE>
+__device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
+                                               const uint32_t (&cw)[E / 4], const Smem& S,
+                                               const unsigned char* table, double* bins, int lane,
+                                               uint8_t* assign_row, uint32_t (&packed)[E / 8],
+                                               int n_valid) {
+#ifndef ANY4_CHUNK
+#define ANY4_CHUNK 8
+#endif
+  constexpr int CH = ANY4_CHUNK;  // elements whose table reads are in flight together
   const float t7 = uniform_f(S.thr[7]);
+  double J = 0.0;
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int pos = sorted_position(x[m], t7, S.thr);
-    double* b = bins + pos * kWave + lane;
-    const double ad = static_cast<double>(a[m]);
-    atomicAdd(b, ad);
-    atomicAdd(b + kMaxClusters * kWave, ad * static_cast<double>(x[m]));
+  for (int m0 = 0; m0 < E; m0 += CH) {
+    // The chunk's registers are re-declared opaque: this keeps the compiler from
+    // hoisting the fp64 conversions of the whole resident row out of the Lloyd loop,
+    // while the CH independent reads of a chunk still overlap.
+#pragma unroll
+    for (int m = m0; m < m0 + CH; ++m) asm volatile("" : "+v"(x[m]), "+v"(a[m]));
+    uint32_t cwc[CH / 4];
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) {
+      cwc[i] = cw[m0 / 4 + i];
+      asm volatile("" : "+v"(cwc[i]));  // keep the packed cells packed between rounds
+    }
+    int pos[CH];
+    if (TABLE) {
+      float4 e[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int m = m0 + i;
+        const uint32_t off = ((cwc[i >> 2] >> (8 * (i & 3))) & 0xFFu) * 16u;
+        e[i] = *reinterpret_cast<const float4*>(table + off);
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const float xm = x[m0 + i];
+        pos[i] = static_cast<int>(__float_as_uint(e[i].z)) + (xm >= e[i].x ? 1 : 0) +
+                 (xm >= e[i].y ? 1 : 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) pos[i] = sorted_position(x[m0 + i], t7, S.thr);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int m = m0 + i;
+      const double ad = static_cast<double>(a[m]);
+      if (KIND != PASS_FINAL) {
+        double* b = bins + pos[i] * kBinCols + (lane & (kBinCols - 1));
+        atomicAdd(b, ad);
+        atomicAdd(b + kMaxClusters * kBinCols, ad * static_cast<double>(x[m]));
+      }
+      if (KIND != PASS_ACCUM) {
+        const int q = S.sidx[pos[i]];
+        const double d = static_cast<double>(x[m]) - static_cast<double>(S.sv[pos[i]]);
+        J += ad * d * d;
+        if (KIND == PASS_STEP && m < n_valid) assign_row[m] = static_cast<uint8_t>(q);
+        if (KIND == PASS_FINAL) packed[m / 8] |= static_cast<uint32_t>(q) << (4 * (m % 8));
+      }
+    }
   }
+  return J;
 }
 
 // Reduce this wave's bins into 32 slot sums (S0[0..15], S1[0..15]) and clear them.
-// Lane l sums slot l>>1 over 32 lanes' partials in a fixed rotated order (rotation
-// keeps the 16-byte reads of 8 consecutive lanes on distinct banks).
+// Lane l sums half of slot l>>1's columns in a fixed rotated order (rotation keeps
+// the 16-byte reads of 8 consecutive lanes on distinct banks).
 __device__ __forceinline__ double reduce_bins(double* bins, int lane) {
+  asm volatile("" : "+v"(lane));  // recompute the addresses per round instead of holding them
+  constexpr int CH = kBinCols / 4;  // double2 chunks per half slot
   const int slot = lane >> 1, half = lane & 1;
-  double2* src = reinterpret_cast<double2*>(bins + slot * kWave + half * 32);
+  double2* src = reinterpret_cast<double2*>(bins + slot * kBinCols + half * (kBinCols / 2));
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int j = (i + lane) & 15;
+  for (int i = 0; i < CH; ++i) {
+    const int j = (i + lane) & (CH - 1);
     const double2 v = src[j];
     s += v.x;
     s += v.y;
     src[j] = make_double2(0.0, 0.0);
   }
-  const double other = __shfl_xor(s, 1);
+  const double other = dppd<0xB1>(s);
   return half ? other + s : s + other;  // same order in both lanes of the pair
 }
 
 __device__ __forceinline__ void zero_bins(double* bins, int lane) {
-  double2* dst = reinterpret_cast<double2*>(bins + lane * 32);
+  asm volatile("" : "+v"(lane));
+  constexpr int PER_LANE = 2 * kMaxClusters * kBinCols / kWave;  // doubles per lane
+  double2* dst = reinterpret_cast<double2*>(bins + lane * PER_LANE);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dst[i] = make_double2(0.0, 0.0);
+  for (int i = 0; i < PER_LANE / 2; ++i) dst[i] = make_double2(0.0, 0.0);
 }
 
 // All-waves step: bins -> S.red (block-wide slot sums).
@@ -483,8 +653,17 @@ __device__ __forceinline__ double block_sum_f64(double v, Smem& S, int lane, int
 }
 
 // ---------------------------------------------------------------------------------
+// Occupancy target per element count: 32 elements per lane fit 3 waves per SIMD;
+// 64 do not (their registers would spill inside the Lloyd loop), so they get no hint.
+template <int E>
+struct WavesPerEU {
+  static constexpr int value = (E == 32) ? 3 : 0;
+};
+
 template <int E, int NWMAX, int MODE>
-__global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArgs args) {
+__global__ __launch_bounds__(kWave* NWMAX)
+__attribute__((amdgpu_waves_per_eu(WavesPerEU<E>::value == 0 ? 1 : WavesPerEU<E>::value)))
+void any4_rows_kernel(const LaunchArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Smem& S = *reinterpret_cast<Smem*>(smem_raw);
   const int nw = (NWMAX == 1) ? 1 : args.nw;
@@ -505,13 +684,14 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
   const float qr = static_cast<float>(k - 1);
   const int col0 = tid * E;
 
+  const int n_valid = (K - col0 < E) ? (K - col0 > 0 ? K - col0 : 0) : E;  // valid columns here
   float xv[E], av[E];
   load_row<E>(M, row, K, col0, xv, av);
 
   bool bad = false;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
-    if (col0 + m < K) {
+    if (m < n_valid) {
       if (!is_finite(xv[m])) bad = true;
       if (!(av[m] >= 0.0f) || !is_finite(av[m])) bad = true;
     }
@@ -534,7 +714,7 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
   if (MODE == MODE_SCALE) {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      if (col0 + m < K) {
+      if (m < n_valid) {
         M.ws_out[row * K + col0 + m] = xv[m];
         M.a_out[row * K + col0 + m] = av[m];
       }
@@ -547,7 +727,7 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
   if (row_bad) {
     if (MODE == MODE_FULL) {
       for (int m = 0; m < E; m += 2)
-        if (col0 + m < K) M.codes[row * (K / 2) + (col0 + m) / 2] = 0;
+        if (m < n_valid) M.codes[row * (K / 2) + (col0 + m) / 2] = 0;
       if (tid < k) M.lut[row * k + tid] = 0;
       // the lanes that wrote alpha/beta of a group overwrite them
       for (int c = col0; c < col0 + E && c < K; c += (g < E ? g : E)) {
@@ -596,10 +776,13 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
         const double sc = ldexp(1.0, 40 - (e2 - 1));  // 2^(40 - floor(log2 pmax))
         double lsum = 0.0;
 #pragma unroll
-        for (int m = 0; m < E; ++m) lsum += floor(static_cast<double>(pv[m]) * sc);
+        for (int m = 0; m < E; ++m) {
+          asm volatile("" : "+v"(pv[m]));  // one fp64 temporary at a time
+          lsum += floor(static_cast<double>(pv[m]) * sc);
+        }
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
-        const unsigned long long incl = wave_incl_scan_u64(ls, lane);
-        unsigned long long woff = 0, Q = __shfl(incl, kWave - 1);
+        const unsigned long long incl = wave_incl_scan_u64(ls);
+        unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
         if (nw > 1) {
           if (lane == kWave - 1) S.ured[t & 1][wave] = incl;
           __syncthreads();
@@ -626,7 +809,7 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
         if (wave == 0) {
           const unsigned long long oex = S.owner_excl;
           const double q = (lane < E) ? floor(static_cast<double>(S.stage_p[lane]) * sc) : 0.0;
-          const double qi = wave_incl_scan_f64(q, lane);
+          const double qi = wave_incl_scan_f64(q);
           const bool hit = lane < E && oex + static_cast<unsigned long long>(qi) > r;
           const unsigned long long bal = __ballot(hit);
           int ms = __ffsll(static_cast<long long>(bal)) - 1;
@@ -647,6 +830,7 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
       // sampling weights for the next draw: a_j * min_t fl((w_S_j - c_t)^2)
 #pragma unroll
       for (int m = 0; m < E; ++m) {
+        asm volatile("" : "+v"(pv[m]));
         float d = xv[m] - ct;
         d = d * d;
         const float pd = av[m] * d;
@@ -665,33 +849,42 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
   }
 
   // ---- Lloyd rounds
-  double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr) + wave * (2 * kMaxClusters * kWave);
+  const int G = kCellsPerUnit * k;
+  uint32_t cw[E / 4];  // table cell of each element, four per register
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i)
+    cw[i] = cell_of(xv[4 * i], G) | (cell_of(xv[4 * i + 1], G) << 8) |
+            (cell_of(xv[4 * i + 2], G) << 16) | (cell_of(xv[4 * i + 3], G) << 24);
+  unsigned char* table = smem_raw + kSmemHdr;
+  double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
+                 wave * (2 * kMaxClusters * kBinCols);
+  const int nthreads = nw * kWave;
+  uint32_t packed[E / 8];
+#pragma unroll
+  for (int v = 0; v < E / 8; ++v) packed[v] = 0;
   zero_bins(bins, lane);
   const int rounds = (MODE == MODE_STEP) ? 1 : args.iters;
   for (int it = 0; it < rounds; ++it) {
-    if (wave == 0) build_structure(S, k, lane);
+    if (wave == 0) build_structure(S, k, G, lane);
     __syncthreads();
+    const bool use_table = !__syncthreads_or(build_table(S, table, G, tid, nthreads));
     if (MODE == MODE_STEP) {
       // E-step with its assignment and objective at c_in, then the same bin sums
-      const float t7 = uniform_f(S.thr[7]);
+      uint8_t* arow = M.assign_out + row * K + col0;
       double J = 0.0;
-#pragma unroll
-      for (int m = 0; m < E; ++m) {
-        const int pos = sorted_position(xv[m], t7, S.thr);
-        double* bp = bins + pos * kWave + lane;
-        const double ad = static_cast<double>(av[m]);
-        atomicAdd(bp, ad);
-        atomicAdd(bp + kMaxClusters * kWave, ad * static_cast<double>(xv[m]));
-        if (col0 + m < K) {
-          M.assign_out[row * K + col0 + m] = static_cast<uint8_t>(S.sidx[pos]);
-          const double d = static_cast<double>(xv[m]) - static_cast<double>(S.sv[pos]);
-          J += static_cast<double>(av[m]) * d * d;
-        }
+      if (col0 < K) {
+        J = use_table ? element_pass<E, PASS_STEP, true>(xv, av, cw, S, table, bins, lane, arow,
+                                                          packed, n_valid)
+                      : element_pass<E, PASS_STEP, false>(xv, av, cw, S, table, bins, lane, arow,
+                                                           packed, n_valid);
       }
       J = block_sum_f64(J, S, lane, wave, nw);
       if (tid == 0 && M.objective) M.objective[row] = J;
-    } else {
-      if (col0 < K) em_pass<E>(xv, av, S, bins, lane);
+    } else if (col0 < K) {
+      if (use_table)
+        element_pass<E, PASS_ACCUM, true>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
+      else
+        element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
     }
     __syncthreads();
     block_reduce_bins(S, bins, lane, wave, nw);
@@ -704,20 +897,15 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
   }
 
   // ---- final E-step, objective and emission
-  if (wave == 0) build_structure(S, k, lane);
+  if (wave == 0) build_structure(S, k, G, lane);
   __syncthreads();
-  const float t7 = uniform_f(S.thr[7]);
+  const bool use_table = !__syncthreads_or(build_table(S, table, G, tid, nthreads));
   double J = 0.0;
-  uint32_t packed[E / 8];
-#pragma unroll
-  for (int v = 0; v < E / 8; ++v) packed[v] = 0;
-#pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int pos = sorted_position(xv[m], t7, S.thr);
-    const uint32_t q = static_cast<uint32_t>(S.sidx[pos]);
-    packed[m / 8] |= q << (4 * (m % 8));
-    const double d = static_cast<double>(xv[m]) - static_cast<double>(S.sv[pos]);
-    J += static_cast<double>(av[m]) * d * d;
+  if (col0 < K) {
+    J = use_table ? element_pass<E, PASS_FINAL, true>(xv, av, cw, S, table, bins, lane, nullptr,
+                                                       packed, n_valid)
+                  : element_pass<E, PASS_FINAL, false>(xv, av, cw, S, table, bins, lane, nullptr,
+                                                        packed, n_valid);
   }
   if (col0 < K) {
     uint8_t* dst = M.codes + row * (K / 2) + col0 / 2;
@@ -731,7 +919,7 @@ __global__ __launch_bounds__(kWave* NWMAX) void any4_rows_kernel(const LaunchArg
     } else {
 #pragma unroll
       for (int m = 0; m < E; m += 2)
-        if (col0 + m < K) dst[m / 2] = static_cast<uint8_t>(packed[m / 8] >> (4 * (m % 8)));
+        if (m < n_valid) dst[m / 2] = static_cast<uint8_t>(packed[m / 8] >> (4 * (m % 8)));
     }
   }
   J = block_sum_f64(J, S, lane, wave, nw);
@@ -770,7 +958,7 @@ template <int E, int NWMAX>
 hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream) {
   const int nw = (NWMAX == 1) ? 1 : args.nw;
   const size_t smem = kSmemHdr + ((mode == MODE_FULL || mode == MODE_STEP)
-                                      ? static_cast<size_t>(nw) * kBinBytesPerWave
+                                      ? kTableBytes + static_cast<size_t>(nw) * kBinBytesPerWave
                                       : 0);
   const dim3 grid(static_cast<unsigned>(n_blocks));
   const dim3 block(kWave * nw);
@@ -795,16 +983,14 @@ hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipSt
 
 }  // namespace
 
+// Launch geometry for a row length, from measurements on the 14336 x 4096 workload:
+// 32 elements per lane (several waves per row) beat one 64-element wave per row,
+// whose register file allows only one wave per SIMD.
 RowConfig choose_config(int64_t K) {
   if (K <= 512) return {8, 1};
   if (K <= 1024) return {16, 1};
-  if (K <= 2048) return {32, 1};
-  if (K <= 4096) return {64, 1};
-  // several waves per row: least padding, then the larger E
-  const int64_t nw64 = (K + 4095) / 4096, nw32 = (K + 2047) / 2048;
-  const int64_t pad64 = nw64 * 4096 - K, pad32 = nw32 * 2048 - K;
-  if (nw32 <= 8 && pad32 < pad64) return {32, static_cast<int>(nw32)};
-  return {64, static_cast<int>(nw64)};
+  if (K <= 16384) return {32, static_cast<int>((K + 2047) / 2048)};
+  return {64, static_cast<int>((K + 4095) / 4096)};
 }
 
 hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t n_blocks,
@@ -820,6 +1006,8 @@ hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t 
     }
   }
   switch (cfg.e) {
+    case 8: return launch_mode<8, 8>(args, mode, n_blocks, stream);
+    case 16: return launch_mode<16, 8>(args, mode, n_blocks, stream);
     case 32: return launch_mode<32, 8>(args, mode, n_blocks, stream);
     case 64: return launch_mode<64, 8>(args, mode, n_blocks, stream);
     default: return hipErrorInvalidValue;
