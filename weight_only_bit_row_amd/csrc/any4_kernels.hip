@@ -16,11 +16,11 @@
 //              Philox4x32-10 draw per (row, step)
 //   Lloyd      per round: sort the <=16 centroids, merge equal values (lowest draw
 //              index kept), compute the exact fp32 switch point between each pair of
-//              sorted neighbours, and tabulate them over fixed 1/16-wide cells of the
-//              scaled range (per cell: cluster position at the cell start and the <= 2
-//              switch points inside it).  Each element's cell is fixed for the whole
-//              row, so its E-step is one LDS table read and two compares; a round
-//              whose table would need a third switch point in one cell uses a 4-level
+//              sorted neighbours, and tabulate them over fixed 1/32-wide cells of the
+//              scaled range (per cell, 8 bytes: cluster position at the cell start and
+//              the switch point inside it).  Each element's cell is fixed for the whole
+//              row, so its E-step is one 8-byte LDS read and one compare; a round whose
+//              table would need a second switch point in one cell uses a 4-level
 //              binary search over all switch points instead (same result).  The
 //              element then adds (a_j, a_j*w_S_j) in fp64 (the product is exact) into
 //              lane-private LDS bins; bins are reduced per wave in a fixed order
@@ -92,9 +92,15 @@ struct Smem {
 };
 
 constexpr size_t kSmemHdr = (sizeof(Smem) + 15) & ~size_t(15);
-constexpr int kCellsPerUnit = 16;                          // cell width 1/16 of a scaled unit
+constexpr int kCellsPerUnit = 32;                          // cell width 1/32 of a scaled unit
 constexpr int kMaxCells = kCellsPerUnit * kMaxClusters;    // cells cover [0, n_clusters)
-constexpr size_t kTableBytes = kMaxCells * 16;             // {T1, T2, position, -} per cell
+constexpr int kCellBytes = 8;                              // {T, position} per cell
+constexpr size_t kTableBytes = kMaxCells * kCellBytes;
+constexpr int kCellsPerWord = 3;                           // 10-bit cell indices packed per register
+template <int E>
+struct CellWords {
+  static constexpr int value = (E + kCellsPerWord - 1) / kCellsPerWord;
+};
 // Lane-private fp64 bins, optionally shared by the lanes l, l + 64/kBinShare, ... of a
 // wave.  Sharers sit in different 16-lane groups of an LDS instruction, so they never
 // collide on a bank within a cycle, and the instruction's fixed lane-group order keeps
@@ -236,7 +242,7 @@ __device__ float switch_point(float cl, int il, float cr, int ir) {
   return __uint_as_float(hi);
 }
 
-// Fixed grid over the scaled range: cell h holds x in [h/16, (h+1)/16).  x * 16 is
+// Fixed grid over the scaled range: cell h holds x in [h/32, (h+1)/32).  x * 32 is
 // exact, so the cell is monotone in x; values past the last cell clamp into it.
 __device__ __forceinline__ uint32_t cell_of(float x, int G) {
   const uint32_t h = static_cast<uint32_t>(x * static_cast<float>(kCellsPerUnit));
@@ -284,9 +290,9 @@ __device__ void build_structure(Smem& S, int k, int G, int lane) {
 
 // All threads: the per-cell table for this round.  For cell h, `position` counts the
 // switch points in earlier cells (all below any x of cell h, by monotonicity of
-// cell_of), and T1 <= T2 are the switch points inside the cell (+inf if none), so the
-// cluster position of x is position + [x >= T1] + [x >= T2].  Returns true when a
-// cell holds a third switch point (the round then uses the binary search).
+// cell_of), and T is the switch point inside the cell (+inf if none), so the cluster
+// position of x is position + [x >= T].  Returns true when a cell holds a second
+// switch point (the round then uses the binary search).
 __device__ __forceinline__ bool build_table(const Smem& S, unsigned char* table, int G, int tid,
                                             int nthreads) {
   constexpr int CPT = kMaxCells / kWave;  // cells per thread with one wave
@@ -311,9 +317,8 @@ __device__ __forceinline__ bool build_table(const Smem& S, unsigned char* table,
     if (h[j] < static_cast<uint32_t>(G)) {
       const int b = base[j];
       const float t1 = (S.tcell[b] == h[j]) ? S.thr[b] : inf;
-      const float t2 = (S.tcell[b + 1] == h[j]) ? S.thr[b + 1] : inf;
-      if (S.tcell[b + 2] == h[j]) over = true;
-      reinterpret_cast<float4*>(table)[h[j]] = make_float4(t1, t2, __uint_as_float(b), 0.0f);
+      if (S.tcell[b + 1] == h[j]) over = true;
+      reinterpret_cast<float2*>(table)[h[j]] = make_float2(t1, __uint_as_float(b));
     }
   }
   return over;
@@ -510,12 +515,12 @@ enum PassKind { PASS_ACCUM = 0, PASS_STEP = 1, PASS_FINAL = 2 };
 
 template <int E, int KIND, bool TABLE>
 __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
-                                               const uint32_t (&cw)[E / 4], const Smem& S,
+                                               const uint32_t (&cw)[CellWords<E>::value], const Smem& S,
                                                const unsigned char* table, double* bins, int lane,
                                                uint8_t* assign_row, uint32_t (&packed)[E / 8],
                                                int n_valid) {
 #ifndef ANY4_CHUNK
-#define ANY4_CHUNK 8
+#define ANY4_CHUNK 4
 #endif
   constexpr int CH = ANY4_CHUNK;  // elements whose table reads are in flight together
   const float t7 = uniform_f(S.thr[7]);
@@ -527,26 +532,30 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
     // while the CH independent reads of a chunk still overlap.
 #pragma unroll
     for (int m = m0; m < m0 + CH; ++m) asm volatile("" : "+v"(x[m]), "+v"(a[m]));
-    uint32_t cwc[CH / 4];
+    // the chunk's packed cell words, re-declared opaque so that they stay packed
+    constexpr int NWC = (CH + kCellsPerWord - 1) / kCellsPerWord + 1;
+    const int W0 = m0 / kCellsPerWord, W1 = (m0 + CH - 1) / kCellsPerWord;
+    uint32_t cwc[NWC];
 #pragma unroll
-    for (int i = 0; i < CH / 4; ++i) {
-      cwc[i] = cw[m0 / 4 + i];
-      asm volatile("" : "+v"(cwc[i]));  // keep the packed cells packed between rounds
+    for (int i = 0; i < NWC; ++i) {
+      if (W0 + i <= W1) {
+        cwc[i] = cw[W0 + i];
+        asm volatile("" : "+v"(cwc[i]));
+      }
     }
     int pos[CH];
     if (TABLE) {
-      float4 e[CH];
+      float2 e[CH];
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int m = m0 + i;
-        const uint32_t off = ((cwc[i >> 2] >> (8 * (i & 3))) & 0xFFu) * 16u;
-        e[i] = *reinterpret_cast<const float4*>(table + off);
+        const uint32_t h = (cwc[m / kCellsPerWord - W0] >> (10 * (m % kCellsPerWord))) & 0x3FFu;
+        e[i] = *reinterpret_cast<const float2*>(table + h * kCellBytes);
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const float xm = x[m0 + i];
-        pos[i] = static_cast<int>(__float_as_uint(e[i].z)) + (xm >= e[i].x ? 1 : 0) +
-                 (xm >= e[i].y ? 1 : 0);
+        pos[i] = static_cast<int>(__float_as_uint(e[i].y)) + (xm >= e[i].x ? 1 : 0);
       }
     } else {
 #pragma unroll
@@ -850,11 +859,11 @@ void any4_rows_kernel(const LaunchArgs args) {
 
   // ---- Lloyd rounds
   const int G = kCellsPerUnit * k;
-  uint32_t cw[E / 4];  // table cell of each element, four per register
+  uint32_t cw[CellWords<E>::value];  // table cell of each element, three per register
 #pragma unroll
-  for (int i = 0; i < E / 4; ++i)
-    cw[i] = cell_of(xv[4 * i], G) | (cell_of(xv[4 * i + 1], G) << 8) |
-            (cell_of(xv[4 * i + 2], G) << 16) | (cell_of(xv[4 * i + 3], G) << 24);
+  for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
+#pragma unroll
+  for (int m = 0; m < E; ++m) cw[m / kCellsPerWord] |= cell_of(xv[m], G) << (10 * (m % kCellsPerWord));
   unsigned char* table = smem_raw + kSmemHdr;
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  wave * (2 * kMaxClusters * kBinCols);
