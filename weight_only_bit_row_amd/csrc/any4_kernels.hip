@@ -73,7 +73,6 @@ struct Smem {
   uint32_t tcell[kMaxClusters + 4];  // cell of each switch point, kMaxCells beyond the last
   float sv[kMaxClusters];     // sorted distinct centroid values
   int sidx[kMaxClusters];     // lowest draw index holding each sorted value
-  double red[2 * kMaxClusters];         // reduced bins: S0[16], S1[16]
   double wred[8][2 * kMaxClusters];     // per-wave partial bins
   float fred[2][8];                     // per-wave fp32 partials (double buffered)
   double dred[8];                       // per-wave fp64 partials
@@ -88,7 +87,9 @@ struct Smem {
   int owner;
   int pick_j;
   int n_unique;
-  int pad_[3];
+  int use_table;                        // this round's cell table is complete
+  uint32_t tbits[kWave];                // switch points of each lane's 8 cells, a bit per cell
+  int pad_[2];
 };
 
 constexpr size_t kSmemHdr = (sizeof(Smem) + 15) & ~size_t(15);
@@ -252,7 +253,8 @@ __device__ __forceinline__ uint32_t cell_of(float x, int G) {
 // Wave 0 only: from S.c (k values), build the sorted distinct values, their lowest
 // draw index, the switch points S.thr[0..U-2] (+inf beyond) and their cells.  The
 // centroids are broadcast to uniform registers; each lane ranks its own centroid.
-__device__ void build_structure(Smem& S, int k, int G, int lane) {
+// Lane t < U - 1 returns switch point t and its cell in (t_out, tc_out); returns U.
+__device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, uint32_t& tc_out) {
   const float inf = __builtin_huge_valf();
   float ct = (lane < k) ? S.c[lane] : inf;
   if (ct == 0.0f) ct = 0.0f;  // -0 -> +0 so that bit patterns order like values
@@ -274,54 +276,70 @@ __device__ void build_structure(Smem& S, int k, int G, int lane) {
     S.sidx[less] = lane;
   }
   wave_lds_fence();
+  float t = inf;
+  uint32_t tc = kMaxCells;
+  if (lane + 1 < U) {
+    t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
+    tc = cell_of(t, G);
+  }
   if (lane < kMaxClusters + 4) {
-    float t = inf;
-    uint32_t tc = kMaxCells;
-    if (lane + 1 < U) {
-      t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
-      tc = cell_of(t, G);
-    }
     S.thr[lane] = t;
     S.tcell[lane] = tc;
   }
   if (lane == 0) S.n_unique = U;
   wave_lds_fence();
+  t_out = t;
+  tc_out = tc;
+  return U;
 }
 
-// All threads: the per-cell table for this round.  For cell h, `position` counts the
-// switch points in earlier cells (all below any x of cell h, by monotonicity of
-// cell_of), and T is the switch point inside the cell (+inf if none), so the cluster
-// position of x is position + [x >= T].  Returns true when a cell holds a second
-// switch point (the round then uses the binary search).
-__device__ __forceinline__ bool build_table(const Smem& S, unsigned char* table, int G, int tid,
-                                            int nthreads) {
-  constexpr int CPT = kMaxCells / kWave;  // cells per thread with one wave
+// exclusive prefix sums of a u32 over the wave's lanes
+__device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
+  uint32_t s = v;
+  s += static_cast<uint32_t>(dpp<0x111>(static_cast<int>(s)));
+  s += static_cast<uint32_t>(dpp<0x112>(static_cast<int>(s)));
+  s += static_cast<uint32_t>(dpp<0x114>(static_cast<int>(s)));
+  s += static_cast<uint32_t>(dpp<0x118>(static_cast<int>(s)));
+  s += static_cast<uint32_t>(dpp<0x142, 0xA>(static_cast<int>(s)));
+  s += static_cast<uint32_t>(dpp<0x143, 0xC>(static_cast<int>(s)));
+  return s - v;
+}
+
+// Wave 0, right after build_structure: the per-cell table for this round.  For cell h,
+// `position` counts the switch points in earlier cells (all below any x of cell h, by
+// monotonicity of cell_of), and T is the switch point inside the cell (+inf if none),
+// so the cluster position of x is position + [x >= T].  Lane l fills cells [8l, 8l+8):
+// each switch point sets its cell's bit in a per-lane bitmap, a prefix sum of the
+// bitmaps' popcounts over the lanes gives the count below each lane's first cell, and
+// popcounts of the bitmap's low bits the rest.  A cell holding a second switch point
+// makes the round use the binary search (S.use_table = 0).
+constexpr int kCellsPerLane = kMaxCells / kWave;
+static_assert(kCellsPerLane == 8, "8 cells per lane bitmap byte");
+__device__ __forceinline__ void build_table(Smem& S, unsigned char* table, int lane, float t,
+                                            uint32_t tc, int U) {
+  const bool owner = lane + 1 < U;
+  S.tbits[lane] = 0u;
+  wave_lds_fence();
+  if (owner) atomicOr(&S.tbits[tc / kCellsPerLane], 1u << (tc % kCellsPerLane));
+  wave_lds_fence();
+  const uint32_t bits = S.tbits[lane];
+  const uint32_t below = wave_excl_scan_u32(static_cast<uint32_t>(__popc(bits)));
   const float inf = __builtin_huge_valf();
-  const uint32_t t7 = S.tcell[7];
-  uint32_t h[CPT];
-  int base[CPT];
+  float4* dst = reinterpret_cast<float4*>(table + lane * kCellsPerLane * kCellBytes);
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    h[j] = static_cast<uint32_t>(tid + j * nthreads);
-    base[j] = (t7 < h[j]) ? 8 : 0;
+  for (int j = 0; j < kCellsPerLane; j += 2) {
+    const uint32_t b0 = below + __popc(bits & ((1u << j) - 1u));
+    const uint32_t b1 = below + __popc(bits & ((1u << (j + 1)) - 1u));
+    dst[j / 2] = make_float4(inf, __uint_as_float(b0), inf, __uint_as_float(b1));
   }
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j] + 3] < h[j]) ? 4 : 0;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j] + 1] < h[j]) ? 2 : 0;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) base[j] += (S.tcell[base[j]] < h[j]) ? 1 : 0;
-  bool over = false;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    if (h[j] < static_cast<uint32_t>(G)) {
-      const int b = base[j];
-      const float t1 = (S.tcell[b] == h[j]) ? S.thr[b] : inf;
-      if (S.tcell[b + 1] == h[j]) over = true;
-      reinterpret_cast<float2*>(table)[h[j]] = make_float2(t1, __uint_as_float(b));
-    }
-  }
-  return over;
+  wave_lds_fence();
+  if (owner) reinterpret_cast<float*>(table)[tc * (kCellBytes / 4)] = t;
+  // the next switch point's cell, from lane + 1 (rows of 16 lanes hold all 15)
+  const uint32_t tc_next = static_cast<uint32_t>(__shfl_down(static_cast<int>(tc), 1));
+  const bool two = owner && lane + 2 < U && tc_next == tc;
+  const bool any_two = __ballot(two) != 0ull;
+  if (lane == 0) S.use_table = any_two ? 0 : 1;
+  wave_lds_fence();
 }
 
 // Cluster position (index into the sorted distinct values) of x: the number of
@@ -549,7 +567,8 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int m = m0 + i;
-        const uint32_t h = (cwc[m / kCellsPerWord - W0] >> (10 * (m % kCellsPerWord))) & 0x3FFu;
+        const uint32_t h =
+            __builtin_amdgcn_ubfe(cwc[m / kCellsPerWord - W0], 10 * (m % kCellsPerWord), 10);
         e[i] = *reinterpret_cast<const float2*>(table + h * kCellBytes);
       }
 #pragma unroll
@@ -611,32 +630,19 @@ __device__ __forceinline__ void zero_bins(double* bins, int lane) {
   for (int i = 0; i < PER_LANE / 2; ++i) dst[i] = make_double2(0.0, 0.0);
 }
 
-// All-waves step: bins -> S.red (block-wide slot sums).
-__device__ __forceinline__ void block_reduce_bins(Smem& S, double* bins, int lane, int wave,
-                                                  int nw) {
-  const double s = reduce_bins(bins, lane);
-  if (nw == 1) {
-    if ((lane & 1) == 0) S.red[lane >> 1] = s;
-    __syncthreads();
-  } else {
-    if ((lane & 1) == 0) S.wred[wave][lane >> 1] = s;
-    __syncthreads();
-    if (wave == 0 && lane < 2 * kMaxClusters) {
-      double t = S.wred[0][lane];
-      for (int w = 1; w < nw; ++w) t += S.wred[w][lane];
-      S.red[lane] = t;
-    }
-    __syncthreads();
+// Wave 0, after every wave has published its reduced bins in S.wred: block-wide slot
+// sums in wave order, then the Eq. 23 update (fp64 ratio rounded to fp32).  Lane p
+// holds S0 of sorted position p and fetches S1 from lane p + 16.  An empty cluster
+// (zero weight) keeps its value.
+__device__ __forceinline__ void update_centroids(Smem& S, int nw, int lane) {
+  double t = 0.0;
+  if (lane < 2 * kMaxClusters) {
+    t = S.wred[0][lane];
+    for (int w = 1; w < nw; ++w) t += S.wred[w][lane];
   }
-}
-
-// Wave 0: Eq. 23 update, the fp64 ratio rounded to fp32; an empty cluster (zero
-// weight) keeps its value.
-__device__ __forceinline__ void update_centroids(Smem& S, int lane, int wave) {
-  if (wave == 0 && lane < S.n_unique) {
-    const double s0 = S.red[lane], s1 = S.red[kMaxClusters + lane];
-    if (s0 > 0.0) S.c[S.sidx[lane]] = static_cast<float>(s1 / s0);
-  }
+  const double s1 = __shfl_down(t, kMaxClusters);
+  if (lane < S.n_unique && t > 0.0) S.c[S.sidx[lane]] = static_cast<float>(s1 / t);
+  wave_lds_fence();
 }
 
 __device__ __forceinline__ float block_max(float v, Smem& S, int lane, int wave, int nw,
@@ -867,16 +873,23 @@ void any4_rows_kernel(const LaunchArgs args) {
   unsigned char* table = smem_raw + kSmemHdr;
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  wave * (2 * kMaxClusters * kBinCols);
-  const int nthreads = nw * kWave;
   uint32_t packed[E / 8];
 #pragma unroll
   for (int v = 0; v < E / 8; ++v) packed[v] = 0;
   zero_bins(bins, lane);
   const int rounds = (MODE == MODE_STEP) ? 1 : args.iters;
+  // Per round: every wave runs its elements and publishes its reduced bins (one
+  // barrier); wave 0 alone updates the centroids and prepares the next round's sorted
+  // values, switch points and cell table (second barrier).
+  if (wave == 0) {
+    float t;
+    uint32_t tc;
+    const int U = build_structure(S, k, G, lane, t, tc);
+    build_table(S, table, lane, t, tc, U);
+  }
+  __syncthreads();
   for (int it = 0; it < rounds; ++it) {
-    if (wave == 0) build_structure(S, k, G, lane);
-    __syncthreads();
-    const bool use_table = !__syncthreads_or(build_table(S, table, G, tid, nthreads));
+    const bool use_table = S.use_table != 0;
     if (MODE == MODE_STEP) {
       // E-step with its assignment and objective at c_in, then the same bin sums
       uint8_t* arow = M.assign_out + row * K + col0;
@@ -895,9 +908,16 @@ void any4_rows_kernel(const LaunchArgs args) {
       else
         element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
     }
+    const double part = reduce_bins(bins, lane);
+    if ((lane & 1) == 0) S.wred[wave][lane >> 1] = part;
     __syncthreads();
-    block_reduce_bins(S, bins, lane, wave, nw);
-    update_centroids(S, lane, wave);
+    if (wave == 0) {
+      update_centroids(S, nw, lane);
+      float t;
+      uint32_t tc;
+      const int U = build_structure(S, k, G, lane, t, tc);
+      build_table(S, table, lane, t, tc, U);
+    }
     __syncthreads();
   }
   if (MODE == MODE_STEP) {
@@ -905,10 +925,8 @@ void any4_rows_kernel(const LaunchArgs args) {
     return;
   }
 
-  // ---- final E-step, objective and emission
-  if (wave == 0) build_structure(S, k, G, lane);
-  __syncthreads();
-  const bool use_table = !__syncthreads_or(build_table(S, table, G, tid, nthreads));
+  // ---- final E-step, objective and emission (structure and table of c^iters are ready)
+  const bool use_table = S.use_table != 0;
   double J = 0.0;
   if (col0 < K) {
     J = use_table ? element_pass<E, PASS_FINAL, true>(xv, av, cw, S, table, bins, lane, nullptr,
