@@ -88,6 +88,7 @@ struct Smem {
   int pick_j;
   int n_unique;
   int use_table;                        // this round's cell table is complete
+  int bad[8];                           // per-wave vote: the row holds a bad value
   uint32_t tbits[kWave];                // switch points of each lane's 8 cells, a bit per cell
   int pad_[2];
 };
@@ -97,11 +98,22 @@ constexpr int kCellsPerUnit = 32;                          // cell width 1/32 of
 constexpr int kMaxCells = kCellsPerUnit * kMaxClusters;    // cells cover [0, n_clusters)
 constexpr int kCellBytes = 8;                              // {T, position} per cell
 constexpr size_t kTableBytes = kMaxCells * kCellBytes;
-constexpr int kCellsPerWord = 3;                           // 10-bit cell indices packed per register
+// Each element keeps the LDS byte address of its table cell in a 16-bit field, two per
+// register, so that its E-step address costs one bit-field operation.
+constexpr int kCellsPerWord = 2;
 template <int E>
 struct CellWords {
   static constexpr int value = (E + kCellsPerWord - 1) / kCellsPerWord;
 };
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+__device__ __forceinline__ uint32_t lds_address(unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_byte*)p));
+}
+__device__ __forceinline__ float2 lds_read_float2(uint32_t a) {
+  const unsigned long long v = *reinterpret_cast<const __attribute__((address_space(3))) unsigned long long*>(
+      static_cast<size_t>(a));
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
 // Lane-private fp64 bins, optionally shared by the lanes l, l + 64/kBinShare, ... of a
 // wave.  Sharers sit in different 16-lane groups of an LDS instruction, so they never
 // collide on a bank within a cycle, and the instruction's fixed lane-group order keeps
@@ -567,9 +579,8 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int m = m0 + i;
-        const uint32_t h =
-            __builtin_amdgcn_ubfe(cwc[m / kCellsPerWord - W0], 10 * (m % kCellsPerWord), 10);
-        e[i] = *reinterpret_cast<const float2*>(table + h * kCellBytes);
+        const uint32_t w = cwc[m / kCellsPerWord - W0];
+        e[i] = lds_read_float2((m % kCellsPerWord) ? (w >> 16) : (w & 0xFFFFu));
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -601,22 +612,24 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
   return J;
 }
 
-// Reduce this wave's bins into 32 slot sums (S0[0..15], S1[0..15]) and clear them.
-// Lane l sums half of slot l>>1's columns in a fixed rotated order (rotation keeps
-// the 16-byte reads of 8 consecutive lanes on distinct banks).
-__device__ __forceinline__ double reduce_bins(double* bins, int lane) {
+// Reduce this wave's bins into 32 slot totals (S0[0..15], S1[0..15]).  The bins are
+// never cleared: they accumulate over the rounds, and a round's sums are this total
+// minus the previous round's (an untouched slot reads back bit-identical, so it gives
+// exactly 0).  Lane l sums half of slot l>>1's columns in a fixed rotated order that puts
+// the 16-byte reads of any 8 or 16 consecutive lanes on distinct banks.
+__device__ __forceinline__ double reduce_bins(const double* bins, int lane) {
   asm volatile("" : "+v"(lane));  // recompute the addresses per round instead of holding them
   constexpr int CH = kBinCols / 4;  // double2 chunks per half slot
   const int slot = lane >> 1, half = lane & 1;
-  double2* src = reinterpret_cast<double2*>(bins + slot * kBinCols + half * (kBinCols / 2));
+  const double2* src =
+      reinterpret_cast<const double2*>(bins + slot * kBinCols + half * (kBinCols / 2));
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int j = (i + lane) & (CH - 1);
+    const int j = (i + (lane >> 1) + (CH / 2) * half) & (CH - 1);
     const double2 v = src[j];
     s += v.x;
     s += v.y;
-    src[j] = make_double2(0.0, 0.0);
   }
   const double other = dppd<0xB1>(s);
   return half ? other + s : s + other;  // same order in both lanes of the pair
@@ -737,8 +750,14 @@ void any4_rows_kernel(const LaunchArgs args) {
     return;
   }
 
+  // a row is rejected when any lane found a bad value (per-wave votes in LDS; the
+  // runtime's block vote would add static shared memory in front of the dynamic one)
   if (tid == 0) S.x0 = xv[0];
-  const bool row_bad = __syncthreads_or(bad);
+  const bool wave_bad = __ballot(bad) != 0ull;
+  if (lane == 0) S.bad[wave] = wave_bad ? 1 : 0;
+  __syncthreads();
+  bool row_bad = false;
+  for (int w = 0; w < nw; ++w) row_bad = row_bad || S.bad[w] != 0;
   if (row_bad) {
     if (MODE == MODE_FULL) {
       for (int m = 0; m < E; m += 2)
@@ -865,18 +884,23 @@ void any4_rows_kernel(const LaunchArgs args) {
 
   // ---- Lloyd rounds
   const int G = kCellsPerUnit * k;
-  uint32_t cw[CellWords<E>::value];  // table cell of each element, three per register
-#pragma unroll
-  for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
-#pragma unroll
-  for (int m = 0; m < E; ++m) cw[m / kCellsPerWord] |= cell_of(xv[m], G) << (10 * (m % kCellsPerWord));
   unsigned char* table = smem_raw + kSmemHdr;
+  uint32_t cw[CellWords<E>::value];  // LDS address of each element's table cell, two per register
+  {
+    const uint32_t tbase = lds_address(table);
+#pragma unroll
+    for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      cw[m / kCellsPerWord] |= (tbase + cell_of(xv[m], G) * kCellBytes) << (16 * (m % kCellsPerWord));
+  }
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  wave * (2 * kMaxClusters * kBinCols);
   uint32_t packed[E / 8];
 #pragma unroll
   for (int v = 0; v < E / 8; ++v) packed[v] = 0;
   zero_bins(bins, lane);
+  double prev_total = 0.0;  // this lane's slot total after the previous round
   const int rounds = (MODE == MODE_STEP) ? 1 : args.iters;
   // Per round: every wave runs its elements and publishes its reduced bins (one
   // barrier); wave 0 alone updates the centroids and prepares the next round's sorted
@@ -908,8 +932,9 @@ void any4_rows_kernel(const LaunchArgs args) {
       else
         element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
     }
-    const double part = reduce_bins(bins, lane);
-    if ((lane & 1) == 0) S.wred[wave][lane >> 1] = part;
+    const double total = reduce_bins(bins, lane);
+    if ((lane & 1) == 0) S.wred[wave][lane >> 1] = total - prev_total;
+    prev_total = total;
     __syncthreads();
     if (wave == 0) {
       update_centroids(S, nw, lane);
