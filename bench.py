@@ -7,6 +7,7 @@ outputs are preallocated.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --profile-steps 3          # short run for rocprofv3
+  python bench.py --profile-steps 2 --iters 0   # same, without Lloyd rounds (counter deltas)
   python bench.py --copy-calibration         # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -108,6 +109,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many quantize calls (for rocprofv3), no baseline")
+    ap.add_argument("--iters", type=int, default=None,
+                    help="Lloyd rounds for --profile-steps runs (default: the workload's 20)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -138,8 +141,9 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_steps:
+        p_iters = iters if args.iters is None else args.iters
         for _ in range(args.profile_steps):
-            any4.quantize(w, act, group=g, n_clusters=k, iters=iters, out=out, ws=ws)
+            any4.quantize(w, act, group=g, n_clusters=k, iters=p_iters, out=out, ws=ws)
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "status": any4.read_status(ws)}))
         return
