@@ -265,8 +265,10 @@ __device__ __forceinline__ uint32_t cell_of(float x, int G) {
 // Wave 0 only: from S.c (k values), build the sorted distinct values, their lowest
 // draw index, the switch points S.thr[0..U-2] (+inf beyond) and their cells.  The
 // centroids are broadcast to uniform registers; each lane ranks its own centroid.
-// Lane t < U - 1 returns switch point t and its cell in (t_out, tc_out); returns U.
-__device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, uint32_t& tc_out) {
+// Lane t < U - 1 returns switch point t and its cell in (t_out, tc_out), lane p < U the
+// sorted value p and its draw index in (sv_out, si_out); returns U.
+__device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, uint32_t& tc_out,
+                               float& sv_out, int& si_out) {
   const float inf = __builtin_huge_valf();
   float ct = (lane < k) ? S.c[lane] : inf;
   if (ct == 0.0f) ct = 0.0f;  // -0 -> +0 so that bit patterns order like values
@@ -294,6 +296,8 @@ __device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, ui
     t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
     tc = cell_of(t, G);
   }
+  sv_out = (lane < U) ? S.sv[lane] : inf;
+  si_out = (lane < U) ? S.sidx[lane] : 0;
   if (lane < kMaxClusters + 4) {
     S.thr[lane] = t;
     S.tcell[lane] = tc;
@@ -643,19 +647,49 @@ __device__ __forceinline__ void zero_bins(double* bins, int lane) {
   for (int i = 0; i < PER_LANE / 2; ++i) dst[i] = make_double2(0.0, 0.0);
 }
 
-// Wave 0, after every wave has published its reduced bins in S.wred: block-wide slot
-// sums in wave order, then the Eq. 23 update (fp64 ratio rounded to fp32).  Lane p
-// holds S0 of sorted position p and fetches S1 from lane p + 16.  An empty cluster
-// (zero weight) keeps its value.
-__device__ __forceinline__ void update_centroids(Smem& S, int nw, int lane) {
-  double t = 0.0;
-  if (lane < 2 * kMaxClusters) {
-    t = S.wred[0][lane];
-    for (int w = 1; w < nw; ++w) t += S.wred[w][lane];
+// Wave 0, after every wave has published its reduced bins in S.wred: the Eq. 23 update
+// and the next round's structure.  Lane p < U holds sorted value p (sv) and its draw
+// index (si) from the previous structure; it sums S0 and S1 of position p over the waves
+// in wave order, divides in fp64 and rounds to fp32 (an empty cluster keeps its value).
+// When every draw index is its own position (U == k) and the new values are still
+// strictly increasing by position, the sorted order and the lowest-index map are
+// unchanged: only the values and the switch points are recomputed, the right neighbour
+// coming from the next lane by DPP.  Otherwise the structure is rebuilt from the
+// draw-order centroids.  Returns U; (t, tc) as in build_structure.
+__device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int G, int lane, int U,
+                                                    float& sv, int& si, float& t,
+                                                    uint32_t& tc) {
+  float cn = sv;
+  if (lane < U) {
+    double s0 = S.wred[0][lane], s1 = S.wred[0][kMaxClusters + lane];
+    for (int w = 1; w < nw; ++w) {
+      s0 += S.wred[w][lane];
+      s1 += S.wred[w][kMaxClusters + lane];
+    }
+    if (s0 > 0.0) cn = static_cast<float>(s1 / s0);
+    S.c[si] = cn;
   }
-  const double s1 = __shfl_down(t, kMaxClusters);
-  if (lane < S.n_unique && t > 0.0) S.c[S.sidx[lane]] = static_cast<float>(s1 / t);
+  const float cnext = dppf<0x101>(cn);  // row_shl:1, value of lane + 1 (lanes < 16)
+  const bool out_of_order = lane + 1 < U && !(cn < cnext);
+  if (U == k && __ballot(out_of_order) == 0ull) {
+    const int inext = dpp<0x101>(si);
+    t = __builtin_huge_valf();
+    tc = kMaxCells;
+    if (lane + 1 < U) {
+      t = switch_point(cn, si, cnext, inext);
+      tc = cell_of(t, G);
+    }
+    sv = cn;
+    if (lane < U) S.sv[lane] = cn;
+    if (lane < kMaxClusters + 4) {
+      S.thr[lane] = t;
+      S.tcell[lane] = tc;
+    }
+    wave_lds_fence();
+    return U;
+  }
   wave_lds_fence();
+  return build_structure(S, k, G, lane, t, tc, sv, si);
 }
 
 __device__ __forceinline__ float block_max(float v, Smem& S, int lane, int wave, int nw,
@@ -905,10 +939,12 @@ void any4_rows_kernel(const LaunchArgs args) {
   // Per round: every wave runs its elements and publishes its reduced bins (one
   // barrier); wave 0 alone updates the centroids and prepares the next round's sorted
   // values, switch points and cell table (second barrier).
+  float sv = 0.0f;  // wave 0: sorted value of position `lane`, its draw index, and U
+  int si = 0, U = 0;
   if (wave == 0) {
     float t;
     uint32_t tc;
-    const int U = build_structure(S, k, G, lane, t, tc);
+    U = build_structure(S, k, G, lane, t, tc, sv, si);
     build_table(S, table, lane, t, tc, U);
   }
   __syncthreads();
@@ -937,10 +973,9 @@ void any4_rows_kernel(const LaunchArgs args) {
     prev_total = total;
     __syncthreads();
     if (wave == 0) {
-      update_centroids(S, nw, lane);
       float t;
       uint32_t tc;
-      const int U = build_structure(S, k, G, lane, t, tc);
+      U = update_and_structure(S, nw, k, G, lane, U, sv, si, t, tc);
       build_table(S, table, lane, t, tc, U);
     }
     __syncthreads();
