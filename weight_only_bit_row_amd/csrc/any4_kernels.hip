@@ -78,8 +78,8 @@ struct Smem {
   double dred[8];                       // per-wave fp64 partials
   unsigned long long ured[2][8];        // per-wave u64 partials (double buffered)
   unsigned long long u[kMaxClusters];   // Philox draw of each seeding step
-  float stage_p[kWave];                 // sampling weights of the lane owning a pick
-  float stage_x[kWave];                 // its scaled values
+  alignas(16) float stage_p[kWave];     // sampling weights of the lane owning a pick
+  alignas(16) float stage_x[kWave];     // its scaled values
   int picks[kMaxClusters];
   unsigned long long owner_excl;
   float x0;                             // w_S of column 0
@@ -825,13 +825,14 @@ void any4_rows_kernel(const LaunchArgs args) {
       S.u[tid] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
     }
     float pv[E];
+    float lmax = 0.0f;  // this lane's largest sampling weight for the coming draw
 #pragma unroll
-    for (int m = 0; m < E; ++m) pv[m] = av[m];
+    for (int m = 0; m < E; ++m) {
+      pv[m] = av[m];
+      lmax = fmaxf(lmax, pv[m]);
+    }
     __syncthreads();
     for (int t = 0; t < k; ++t) {
-      float lmax = 0.0f;
-#pragma unroll
-      for (int m = 0; m < E; ++m) lmax = fmaxf(lmax, pv[m]);
       const float pmax = block_max(lmax, S, lane, wave, nw, t & 1);
       float ct;
       int pick;
@@ -864,17 +865,21 @@ void any4_rows_kernel(const LaunchArgs args) {
         const unsigned long long excl = woff + incl - ls;
         const unsigned long long r = __umul64hi(S.u[t], Q);
         const bool own = ls > 0 && excl <= r && r - excl < ls;
-        if (own) {
-          S.owner = tid;
-          S.owner_excl = excl;
+        // the owner's wave finds the element: the owner lane stages its weights and
+        // values, and lane m of that wave takes element m (one wave, so no block barrier)
+        if (__ballot(own) != 0ull) {
+          if (own) {
+            S.owner = tid;
+            S.owner_excl = excl;
 #pragma unroll
-          for (int m = 0; m < E; ++m) {
-            S.stage_p[m] = pv[m];
-            S.stage_x[m] = xv[m];
+            for (int v = 0; v < E / 4; ++v) {
+              reinterpret_cast<float4*>(S.stage_p)[v] =
+                  make_float4(pv[4 * v], pv[4 * v + 1], pv[4 * v + 2], pv[4 * v + 3]);
+              reinterpret_cast<float4*>(S.stage_x)[v] =
+                  make_float4(xv[4 * v], xv[4 * v + 1], xv[4 * v + 2], xv[4 * v + 3]);
+            }
           }
-        }
-        __syncthreads();
-        if (wave == 0) {
+          wave_lds_fence();
           const unsigned long long oex = S.owner_excl;
           const double q = (lane < E) ? floor(static_cast<double>(S.stage_p[lane]) * sc) : 0.0;
           const double qi = wave_incl_scan_f64(q);
@@ -891,6 +896,7 @@ void any4_rows_kernel(const LaunchArgs args) {
         ct = S.pick_c;
         pick = S.pick_j;
       }
+      lmax = 0.0f;
       if (tid == 0) {
         S.c[t] = ct;
         S.picks[t] = pick;
@@ -903,6 +909,7 @@ void any4_rows_kernel(const LaunchArgs args) {
         d = d * d;
         const float pd = av[m] * d;
         pv[m] = (t == 0) ? pd : fminf(pv[m], pd);
+        lmax = fmaxf(lmax, pv[m]);
       }
     }
     __syncthreads();
