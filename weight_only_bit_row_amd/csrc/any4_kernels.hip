@@ -89,12 +89,11 @@ struct Smem {
   int n_unique;
   int use_table;                        // this round's cell table is complete
   int bad[8];                           // per-wave vote: the row holds a bad value
-  uint32_t tbits[kWave];                // switch points of each lane's 8 cells, a bit per cell
   int pad_[2];
 };
 
 constexpr size_t kSmemHdr = (sizeof(Smem) + 15) & ~size_t(15);
-constexpr int kCellsPerUnit = 32;                          // cell width 1/32 of a scaled unit
+constexpr int kCellsPerUnit = 2;                           // cell width 1/2 of a scaled unit
 constexpr int kMaxCells = kCellsPerUnit * kMaxClusters;    // cells cover [0, n_clusters)
 constexpr int kCellBytes = 8;                              // {T, position} per cell
 constexpr size_t kTableBytes = kMaxCells * kCellBytes;
@@ -255,8 +254,10 @@ __device__ float switch_point(float cl, int il, float cr, int ir) {
   return __uint_as_float(hi);
 }
 
-// Fixed grid over the scaled range: cell h holds x in [h/32, (h+1)/32).  x * 32 is
-// exact, so the cell is monotone in x; values past the last cell clamp into it.
+// Fixed grid over the scaled range: cell h holds x in [h/2, (h+1)/2).  x * 2 is exact,
+// so the cell is monotone in x; values past the last cell clamp into it.  With at most
+// 32 cells of 8 bytes the whole table spans each LDS bank pair once, so the gathers of
+// the E-step are free of bank conflicts (equal cells are broadcast).
 __device__ __forceinline__ uint32_t cell_of(float x, int G) {
   const uint32_t h = static_cast<uint32_t>(x * static_cast<float>(kCellsPerUnit));
   return h < static_cast<uint32_t>(G) ? h : static_cast<uint32_t>(G - 1);
@@ -324,37 +325,28 @@ __device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
 // Wave 0, right after build_structure: the per-cell table for this round.  For cell h,
 // `position` counts the switch points in earlier cells (all below any x of cell h, by
 // monotonicity of cell_of), and T is the switch point inside the cell (+inf if none),
-// so the cluster position of x is position + [x >= T].  Lane l fills cells [8l, 8l+8):
-// each switch point sets its cell's bit in a per-lane bitmap, a prefix sum of the
-// bitmaps' popcounts over the lanes gives the count below each lane's first cell, and
-// popcounts of the bitmap's low bits the rest.  A cell holding a second switch point
-// makes the round use the binary search (S.use_table = 0).
-constexpr int kCellsPerLane = kMaxCells / kWave;
-static_assert(kCellsPerLane == 8, "8 cells per lane bitmap byte");
+// so the cluster position of x is position + [x >= T].  The switch points' cells are
+// OR-ed into a 32-bit mask across the wave; lane h < 32 fills cell h with the popcount
+// of the mask below it, then each switch point writes itself into its cell.  A cell
+// holding two switch points (the mask then has fewer bits than switch points) makes the
+// round use the binary search (S.use_table = 0).
+static_assert(kMaxCells <= 32, "one mask bit per cell");
 __device__ __forceinline__ void build_table(Smem& S, unsigned char* table, int lane, float t,
                                             uint32_t tc, int U) {
   const bool owner = lane + 1 < U;
-  S.tbits[lane] = 0u;
-  wave_lds_fence();
-  if (owner) atomicOr(&S.tbits[tc / kCellsPerLane], 1u << (tc % kCellsPerLane));
-  wave_lds_fence();
-  const uint32_t bits = S.tbits[lane];
-  const uint32_t below = wave_excl_scan_u32(static_cast<uint32_t>(__popc(bits)));
-  const float inf = __builtin_huge_valf();
-  float4* dst = reinterpret_cast<float4*>(table + lane * kCellsPerLane * kCellBytes);
-#pragma unroll
-  for (int j = 0; j < kCellsPerLane; j += 2) {
-    const uint32_t b0 = below + __popc(bits & ((1u << j) - 1u));
-    const uint32_t b1 = below + __popc(bits & ((1u << (j + 1)) - 1u));
-    dst[j / 2] = make_float4(inf, __uint_as_float(b0), inf, __uint_as_float(b1));
+  uint32_t m = owner ? (1u << tc) : 0u;  // switch points are in lanes 0..14 (one DPP row)
+  m |= static_cast<uint32_t>(dpp<0x111>(static_cast<int>(m)));  // row_shr:1
+  m |= static_cast<uint32_t>(dpp<0x112>(static_cast<int>(m)));  // row_shr:2
+  m |= static_cast<uint32_t>(dpp<0x114>(static_cast<int>(m)));  // row_shr:4
+  m |= static_cast<uint32_t>(dpp<0x118>(static_cast<int>(m)));  // row_shr:8
+  const uint32_t mask = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(m), 15));
+  if (lane < kMaxCells) {
+    const uint32_t below = __popc(mask & ((1u << lane) - 1u));
+    reinterpret_cast<float2*>(table)[lane] = make_float2(__builtin_huge_valf(), __uint_as_float(below));
   }
   wave_lds_fence();
   if (owner) reinterpret_cast<float*>(table)[tc * (kCellBytes / 4)] = t;
-  // the next switch point's cell, from lane + 1 (rows of 16 lanes hold all 15)
-  const uint32_t tc_next = static_cast<uint32_t>(__shfl_down(static_cast<int>(tc), 1));
-  const bool two = owner && lane + 2 < U && tc_next == tc;
-  const bool any_two = __ballot(two) != 0ull;
-  if (lane == 0) S.use_table = any_two ? 0 : 1;
+  if (lane == 0) S.use_table = (__popc(mask) == U - 1) ? 1 : 0;
   wave_lds_fence();
 }
 
