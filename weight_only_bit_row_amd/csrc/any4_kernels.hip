@@ -97,9 +97,10 @@ constexpr int kCellsPerUnit = 2;                           // cell width 1/2 of 
 constexpr int kMaxCells = kCellsPerUnit * kMaxClusters;    // cells cover [0, n_clusters)
 constexpr int kCellBytes = 8;                              // {T, position} per cell
 constexpr size_t kTableBytes = kMaxCells * kCellBytes;
-// Each element keeps the LDS byte address of its table cell in a 16-bit field, two per
-// register, so that its E-step address costs one bit-field operation.
-constexpr int kCellsPerWord = 2;
+// Each element keeps the byte offset of its table cell (cell * 8 < 256) in an 8-bit
+// field, four per register; its E-step address is that byte plus the table's LDS base.
+constexpr int kCellsPerWord = 4;
+static_assert(kMaxCells * kCellBytes <= 256, "cell offsets fit a byte");
 template <int E>
 struct CellWords {
   static constexpr int value = (E + kCellsPerWord - 1) / kCellsPerWord;
@@ -550,6 +551,7 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
 #endif
   constexpr int CH = ANY4_CHUNK;  // elements whose table reads are in flight together
   const float t7 = uniform_f(S.thr[7]);
+  const uint32_t tbase = lds_address(const_cast<unsigned char*>(table));
   double J = 0.0;
 #pragma unroll
   for (int m0 = 0; m0 < E; m0 += CH) {
@@ -576,7 +578,7 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
       for (int i = 0; i < CH; ++i) {
         const int m = m0 + i;
         const uint32_t w = cwc[m / kCellsPerWord - W0];
-        e[i] = lds_read_float2((m % kCellsPerWord) ? (w >> 16) : (w & 0xFFFFu));
+        e[i] = lds_read_float2(tbase + ((w >> (8 * (m % kCellsPerWord))) & 0xFFu));
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -714,7 +716,10 @@ struct WavesPerEU {
   static constexpr int value = (E == 32) ? 3 : 0;
 };
 
-template <int E, int NWMAX, int MODE>
+// WIDE: the group is at least as wide as a lane's E columns (one group per lane); the
+// kernel is instantiated separately for narrower groups so that neither carries the
+// other's scaling code.
+template <int E, int NWMAX, int MODE, bool WIDE>
 __global__ __launch_bounds__(kWave* NWMAX)
 __attribute__((amdgpu_waves_per_eu(WavesPerEU<E>::value == 0 ? 1 : WavesPerEU<E>::value)))
 void any4_rows_kernel(const LaunchArgs args) {
@@ -752,7 +757,7 @@ void any4_rows_kernel(const LaunchArgs args) {
   }
 
   // ---- Eq. 1-2 scaling and Eq. 23 sample weights
-  if (g >= E) {
+  if constexpr (WIDE) {
     scale_wide<E, MODE>(xv, av, qr, K, col0, bad, M, row, g, S, lane, wave, nw);
   } else {
     switch (g) {
@@ -918,15 +923,12 @@ void any4_rows_kernel(const LaunchArgs args) {
   // ---- Lloyd rounds
   const int G = kCellsPerUnit * k;
   unsigned char* table = smem_raw + kSmemHdr;
-  uint32_t cw[CellWords<E>::value];  // LDS address of each element's table cell, two per register
-  {
-    const uint32_t tbase = lds_address(table);
+  uint32_t cw[CellWords<E>::value];  // byte offset of each element's table cell, four per register
 #pragma unroll
-    for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
+  for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
 #pragma unroll
-    for (int m = 0; m < E; ++m)
-      cw[m / kCellsPerWord] |= (tbase + cell_of(xv[m], G) * kCellBytes) << (16 * (m % kCellsPerWord));
-  }
+  for (int m = 0; m < E; ++m)
+    cw[m / kCellsPerWord] |= (cell_of(xv[m], G) * kCellBytes) << (8 * (m % kCellsPerWord));
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  wave * (2 * kMaxClusters * kBinCols);
   uint32_t packed[E / 8];
@@ -1048,18 +1050,35 @@ hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipSt
                                       : 0);
   const dim3 grid(static_cast<unsigned>(n_blocks));
   const dim3 block(kWave * nw);
+  const bool wide = args.group >= E;
   switch (mode) {
     case MODE_FULL:
-      hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_FULL>), grid, block, smem, stream, args);
+      if (wide)
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_FULL, true>), grid, block, smem, stream, args);
+      else
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_FULL, false>), grid, block, smem, stream,
+                           args);
       break;
     case MODE_SCALE:
-      hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SCALE>), grid, block, smem, stream, args);
+      if (wide)
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SCALE, true>), grid, block, smem, stream, args);
+      else
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SCALE, false>), grid, block, smem, stream,
+                           args);
       break;
     case MODE_SEED:
-      hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SEED>), grid, block, smem, stream, args);
+      if (wide)
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SEED, true>), grid, block, smem, stream, args);
+      else
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SEED, false>), grid, block, smem, stream,
+                           args);
       break;
     case MODE_STEP:
-      hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_STEP>), grid, block, smem, stream, args);
+      if (wide)
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_STEP, true>), grid, block, smem, stream, args);
+      else
+        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_STEP, false>), grid, block, smem, stream,
+                           args);
       break;
     default:
       return hipErrorInvalidValue;
