@@ -840,12 +840,9 @@ void any4_rows_kernel(const LaunchArgs args) {
         int e2;
         frexpf(pmax, &e2);
         const double sc = ldexp(1.0, 40 - (e2 - 1));  // 2^(40 - floor(log2 pmax))
-        double lsum = 0.0;
+        double lsum = floor(static_cast<double>(pv[0]) * sc);
 #pragma unroll
-        for (int m = 0; m < E; ++m) {
-          asm volatile("" : "+v"(pv[m]));  // one fp64 temporary at a time
-          lsum += floor(static_cast<double>(pv[m]) * sc);
-        }
+        for (int m = 1; m < E; ++m) lsum += floor(static_cast<double>(pv[m]) * sc);
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
         const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
@@ -893,21 +890,35 @@ void any4_rows_kernel(const LaunchArgs args) {
         ct = S.pick_c;
         pick = S.pick_j;
       }
-      lmax = 0.0f;
       if (tid == 0) {
         S.c[t] = ct;
         S.picks[t] = pick;
       }
-      // sampling weights for the next draw: a_j * min_t fl((w_S_j - c_t)^2)
+      if (t == k - 1) break;  // the last centroid needs no further sampling weights
+      // sampling weights for the next draw: a_j * min_t fl((w_S_j - c_t)^2).  They are
+      // never NaN and never below zero (a zero may be -0), so the float order is the
+      // order of their bit patterns as signed integers: min and max run as integer ops,
+      // which need no NaN quieting of their operands.
+      int imax = 0;
+      if (t == 0) {
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
-        asm volatile("" : "+v"(pv[m]));
-        float d = xv[m] - ct;
-        d = d * d;
-        const float pd = av[m] * d;
-        pv[m] = (t == 0) ? pd : fminf(pv[m], pd);
-        lmax = fmaxf(lmax, pv[m]);
+        for (int m = 0; m < E; ++m) {
+          float d = xv[m] - ct;
+          d = d * d;
+          pv[m] = av[m] * d;
+          imax = max(imax, __float_as_int(pv[m]));
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          float d = xv[m] - ct;
+          d = d * d;
+          const int pd = __float_as_int(av[m] * d);
+          pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
+          imax = max(imax, __float_as_int(pv[m]));
+        }
       }
+      lmax = __int_as_float(imax);
     }
     __syncthreads();
     if (MODE == MODE_SEED) {
