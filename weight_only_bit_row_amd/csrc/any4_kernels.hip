@@ -540,12 +540,21 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], float
 // FINAL packs the codes and sums the objective.
 enum PassKind { PASS_ACCUM = 0, PASS_STEP = 1, PASS_FINAL = 2 };
 
+// fp64 conversion tied to the round index `tok` (an operand the instruction ignores):
+// the compiler cannot move it out of the round loop, where the conversions of the whole
+// resident row would stay live in 128 registers, and needs no copy of the source.
+__device__ __forceinline__ double cvt_f64_in_round(float v, int tok) {
+  double r;
+  asm("v_cvt_f64_f32 %0, %1" : "=v"(r) : "v"(v), "s"(tok));
+  return r;
+}
+
 template <int E, int KIND, bool TABLE>
 __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
                                                const uint32_t (&cw)[CellWords<E>::value], const Smem& S,
                                                const unsigned char* table, double* bins, int lane,
                                                uint8_t* assign_row, uint32_t (&packed)[E / 8],
-                                               int n_valid) {
+                                               int n_valid, int tok) {
 #ifndef ANY4_CHUNK
 #define ANY4_CHUNK 4
 #endif
@@ -555,12 +564,8 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
   double J = 0.0;
 #pragma unroll
   for (int m0 = 0; m0 < E; m0 += CH) {
-    // The chunk's registers are re-declared opaque: this keeps the compiler from
-    // hoisting the fp64 conversions of the whole resident row out of the Lloyd loop,
-    // while the CH independent reads of a chunk still overlap.
-#pragma unroll
-    for (int m = m0; m < m0 + CH; ++m) asm volatile("" : "+v"(x[m]), "+v"(a[m]));
-    // the chunk's packed cell words, re-declared opaque so that they stay packed
+    // the chunk's packed cell words, re-declared opaque so that they stay packed (their
+    // table addresses are not hoisted out of the round loop into 32 registers)
     constexpr int NWC = (CH + kCellsPerWord - 1) / kCellsPerWord + 1;
     const int W0 = m0 / kCellsPerWord, W1 = (m0 + CH - 1) / kCellsPerWord;
     uint32_t cwc[NWC];
@@ -592,15 +597,16 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int m = m0 + i;
-      const double ad = static_cast<double>(a[m]);
+      const double ad = cvt_f64_in_round(a[m], tok);
+      const double xd = cvt_f64_in_round(x[m], tok);
       if (KIND != PASS_FINAL) {
         double* b = bins + pos[i] * kBinCols + (lane & (kBinCols - 1));
         atomicAdd(b, ad);
-        atomicAdd(b + kMaxClusters * kBinCols, ad * static_cast<double>(x[m]));
+        atomicAdd(b + kMaxClusters * kBinCols, ad * xd);
       }
       if (KIND != PASS_ACCUM) {
         const int q = S.sidx[pos[i]];
-        const double d = static_cast<double>(x[m]) - static_cast<double>(S.sv[pos[i]]);
+        const double d = xd - static_cast<double>(S.sv[pos[i]]);
         J += ad * d * d;
         if (KIND == PASS_STEP && m < n_valid) assign_row[m] = static_cast<uint8_t>(q);
         if (KIND == PASS_FINAL) packed[m / 8] |= static_cast<uint32_t>(q) << (4 * (m % 8));
@@ -968,17 +974,17 @@ void any4_rows_kernel(const LaunchArgs args) {
       double J = 0.0;
       if (col0 < K) {
         J = use_table ? element_pass<E, PASS_STEP, true>(xv, av, cw, S, table, bins, lane, arow,
-                                                          packed, n_valid)
+                                                          packed, n_valid, it)
                       : element_pass<E, PASS_STEP, false>(xv, av, cw, S, table, bins, lane, arow,
-                                                           packed, n_valid);
+                                                           packed, n_valid, it);
       }
       J = block_sum_f64(J, S, lane, wave, nw);
       if (tid == 0 && M.objective) M.objective[row] = J;
     } else if (col0 < K) {
       if (use_table)
-        element_pass<E, PASS_ACCUM, true>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
+        element_pass<E, PASS_ACCUM, true>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
       else
-        element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid);
+        element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
     }
     const double total = reduce_bins(bins, lane);
     if ((lane & 1) == 0) S.wred[wave][lane >> 1] = total - prev_total;
@@ -1002,9 +1008,9 @@ void any4_rows_kernel(const LaunchArgs args) {
   double J = 0.0;
   if (col0 < K) {
     J = use_table ? element_pass<E, PASS_FINAL, true>(xv, av, cw, S, table, bins, lane, nullptr,
-                                                       packed, n_valid)
+                                                       packed, n_valid, rounds)
                   : element_pass<E, PASS_FINAL, false>(xv, av, cw, S, table, bins, lane, nullptr,
-                                                        packed, n_valid);
+                                                        packed, n_valid, rounds);
   }
   if (col0 < K) {
     uint8_t* dst = M.codes + row * (K / 2) + col0 / 2;
