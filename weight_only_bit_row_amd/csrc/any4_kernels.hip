@@ -236,12 +236,26 @@ __device__ __forceinline__ bool right_wins(float x, float cl, int il, float cr, 
 
 // Smallest fp32 x in [cl, cr] (0 <= cl < cr) at which R wins.  The rule is monotone
 // in x on that interval (left distance non-decreasing, right non-increasing under
-// monotone rounding), so a bisection over the ordered bit patterns is exact.  The
-// midpoint probe narrows the interval to a few ulps first.
+// monotone rounding), so the winners form a suffix of the ordered bit patterns.  The
+// answer lies within a few ulps of the rounded midpoint: the five patterns mb-2..mb+2
+// are tested independently, and when mb-2 loses and mb+2 wins the answer is mb-2 plus
+// the number of losers.  Otherwise a bisection over the bit patterns decides (exact).
 __device__ float switch_point(float cl, int il, float cr, int ir) {
   uint32_t lo = __float_as_uint(cl), hi = __float_as_uint(cr);
   const float mid = cl + 0.5f * (cr - cl);
   const uint32_t mb = __float_as_uint(mid);
+  if (mb >= lo + 2 && mb + 2 <= hi) {
+    uint32_t losers = 0;
+    bool w0 = false, w4 = false;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const bool w = right_wins(__uint_as_float(mb - 2 + j), cl, il, cr, ir);
+      losers += w ? 0u : 1u;
+      if (j == 0) w0 = w;
+      if (j == 4) w4 = w;
+    }
+    if (!w0 && w4) return __uint_as_float(mb - 2 + losers);
+  }
   if (mb >= lo + 2 && !right_wins(__uint_as_float(mb - 2), cl, il, cr, ir)) lo = mb - 1;
   if (mb + 2 <= hi && right_wins(__uint_as_float(mb + 2), cl, il, cr, ir)) hi = mb + 2;
   // invariant: every x below lo loses (or lo == cl), and hi wins (or hi == cr)
