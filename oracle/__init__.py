@@ -56,6 +56,13 @@ def lib():
         L.oracle_any4_quantize.argtypes = [P, i32, i64, i64, P, i64, i32, i32, i32, i32, u64,
                                            P, P, P, P, P, P, P, P, P]
         L.oracle_any4_quantize.restype = ctypes.c_int
+        L.oracle_fp16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_fp16_to_f32.restype = ctypes.c_float
+        L.oracle_bf16_rne_array.argtypes = [P, P, i64]
+        L.oracle_act_absmean.argtypes = [P, i32, i64, i64, P]
+        L.oracle_act_absmean.restype = ctypes.c_int
+        L.oracle_dequantize.argtypes = [P, P, P, P, i64, i64, i32, i32, P]
+        L.oracle_dequantize.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -90,6 +97,46 @@ def fp16_bits(x) -> np.ndarray:
     x = _f32(x).reshape(-1)
     out = np.zeros(x.shape, np.uint16)
     lib().oracle_fp16_rne_array(_p(x), _p(out), x.size)
+    return out
+
+
+def fp16_to_f32(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
+    return np.array([lib().oracle_fp16_to_f32(int(v)) for v in b], np.float32)
+
+
+def bf16_bits(x) -> np.ndarray:
+    x = _f32(x)
+    out = np.zeros(x.shape, np.uint16)
+    lib().oracle_bf16_rne_array(_p(x), _p(out), x.size)
+    return out
+
+
+# --- bookends: the calibration statistic and dequantization -----------------------
+
+def act_absmean(x: np.ndarray, dtype: int) -> np.ndarray:
+    """E|x_j| over the rows of x ([T, K]; float32, or uint16 holding bfloat16 bits)."""
+    x = np.ascontiguousarray(x)
+    assert x.dtype == (np.float32 if dtype == 0 else np.uint16) and x.ndim == 2
+    T, K = x.shape
+    out = np.zeros(K, np.float32)
+    st = lib().oracle_act_absmean(_p(x), dtype, T, K, _p(out))
+    if st != 0:
+        raise ValueError("oracle_act_absmean: invalid argument")
+    return out
+
+
+def dequantize(codes, lut, scale, offset, group: int, n_clusters: int) -> np.ndarray:
+    """Eq. 4 dequantization to fp32 [N, K] from the emitted codes/LUT/scale/offset
+    (fp16 arrays may be float16 or their uint16 bits)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    lut, scale, offset = (np.ascontiguousarray(np.asarray(a).view(np.uint16)) for a in (lut, scale, offset))
+    N, K = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((N, K), np.float32)
+    st = lib().oracle_dequantize(_p(codes), _p(lut), _p(scale), _p(offset), N, K, group,
+                                 n_clusters, _p(out))
+    if st != 0:
+        raise ValueError("oracle_dequantize: invalid argument")
     return out
 
 

@@ -19,7 +19,9 @@
  *
  * Pinned by tests/test_oracle_*.py (closed forms, brute-force / DP optimum,
  * scikit-learn Lloyd, numpy Philox4x64, numpy float16 casts, the storage cost
- * printed in Section 2.4.1).  Philox4x32-10's round constants are pinned only
+ * printed in Section 2.4.1; for the bookends E|x| and Eq. 4 dequantization, exact
+ * rational means, a worked example, exact reconstruction of exact-level rows and
+ * torch's bfloat16 cast).  Philox4x32-10's round constants are pinned only
  * through the shared round structure (Philox4x64-10 vs numpy) and a uniformity
  * test: its absolute stream is "parity unpinned".
  */
@@ -386,4 +388,96 @@ int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n
     }
     free(wrow); free(ws); free(a); free(alpha); free(beta); free(q);
     return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Bookends of the quantizer: the calibration statistic it consumes and the
+ * dequantization of what it emits. */
+
+/* IEEE binary16 bit pattern to binary32 (exact: every fp16 value is an fp32 value).
+ * Sign, 5-bit exponent with bias 15, 10-bit fraction; exponent 0 holds zero and the
+ * subnormals (fraction * 2^-24), exponent 31 holds inf and NaN. */
+static float fp16_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu;
+    const uint32_t f = h & 0x3FFu;
+    float mag;
+    if (e == 0) {
+        mag = (float)f * 0x1p-24f;                       /* zero or subnormal, exact */
+    } else if (e == 0x1F) {
+        uint32_t x = 0x7F800000u | (f << 13);            /* inf, or NaN keeping its payload */
+        memcpy(&mag, &x, 4);
+    } else {
+        uint32_t x = ((e - 15 + 127) << 23) | (f << 13);  /* normal: rebias the exponent */
+        memcpy(&mag, &x, 4);
+    }
+    uint32_t bits;
+    memcpy(&bits, &mag, 4);
+    bits |= sign;
+    float out;
+    memcpy(&out, &bits, 4);
+    return out;
+}
+
+float oracle_fp16_to_f32(uint16_t h) { return fp16_to_f32(h); }
+
+/* binary32 to bfloat16 (the upper 16 bits) with round-to-nearest-even on the
+ * discarded 16 bits; NaN stays a quiet NaN. */
+static uint16_t bf16_rne(float f) {
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    if ((x & 0x7F800000u) == 0x7F800000u && (x & 0x7FFFFFu)) return (uint16_t)((x >> 16) | 0x40u);
+    const uint32_t keep = x >> 16, rest = x & 0xFFFFu;
+    uint32_t r = keep;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) r += 1;   /* may carry to inf */
+    return (uint16_t)r;
+}
+
+void oracle_bf16_rne_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne(in[i]);
+}
+
+/* E|x_j| of Section 4.1: the mean over the calibration tokens of the absolute
+ * activation of input channel j.  x is [T, K] row-major (token t, channel j), fp32
+ * (dtype 0) or bf16 bits (dtype 1).  Each channel's |x| values are summed in fp64
+ * in token order, the sum is divided by T in fp64 and rounded to fp32.
+ * Returns 1 for T < 1 or K < 1. */
+int oracle_act_absmean(const void* x, int32_t dtype, int64_t T, int64_t K, float* out) {
+    if (T < 1 || K < 1 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_INVALID_ARG;
+    for (int64_t j = 0; j < K; ++j) {
+        double s = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const float v = dtype == 0 ? ((const float*)x)[t * K + j]
+                                       : bf16_to_f32(((const uint16_t*)x)[t * K + j]);
+            s += fabs((double)v);
+        }
+        out[j] = (float)(s / (double)T);
+    }
+    return ORACLE_OK;
+}
+
+/* Dequantization, Section 2.5.2 (Eq. 4): dequant(w_Q) = alpha * w_Q + beta, where for
+ * any4 the rounded value w_Q of element (i, j) is the row's LUT entry at its code.
+ * The fp16 LUT, scale (alpha) and offset (beta) are widened to fp32 and the value is
+ * fl(fl(alpha * LUT[q]) + beta) in fp32, product and sum rounded separately.
+ * codes [N, K/2] (byte m: column 2m in the low nibble), lut [N, k], scale and
+ * offset [N, K/group]; out [N, K] fp32. */
+int oracle_dequantize(const uint8_t* codes, const uint16_t* lut, const uint16_t* scale,
+                      const uint16_t* offset, int64_t N, int64_t K, int32_t group,
+                      int32_t k, float* out) {
+    if (N < 0 || K < 2 || (K & 1) || group < 1 || K % group != 0 || k < 1 || k > 16)
+        return ORACLE_ERR_INVALID_ARG;
+    const int64_t G = K / group;
+    for (int64_t i = 0; i < N; ++i) {
+        for (int64_t j = 0; j < K; ++j) {
+            const uint8_t byte = codes[i * (K / 2) + j / 2];
+            const int q = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+            const float level = q < k ? fp16_to_f32(lut[i * k + q]) : NAN;
+            const float alpha = fp16_to_f32(scale[i * G + j / group]);
+            const float beta = fp16_to_f32(offset[i * G + j / group]);
+            const float prod = alpha * level;
+            out[i * K + j] = prod + beta;
+        }
+    }
+    return ORACLE_OK;
 }

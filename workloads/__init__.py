@@ -158,6 +158,40 @@ def make(name: str, rows: Optional[int] = None) -> Workload:
     raise KeyError(name)
 
 
+def draw_activations(rng: np.random.Generator, n_tokens: int, profile: np.ndarray,
+                     dtype: int = BF16, chunk: int = 8192) -> np.ndarray:
+    """Calibration activations [T, K]: x_tj = s_j * l_tj with l ~ Laplace(0, 1), whose
+    mean absolute value is 1, so E|x_j| is close to the profile s_j (an E|x| profile from
+    draw_act: lognormal channels with outlier channels x20).  Drawn in row chunks of
+    ``chunk`` tokens (float64, scaled, cast to float32, then to bfloat16 with RNE)."""
+    k = profile.shape[0]
+    s = profile.astype(np.float64)
+    out = np.empty((n_tokens, k), np.float32 if dtype == F32 else np.uint16)
+    for t0 in range(0, n_tokens, chunk):
+        t1 = min(n_tokens, t0 + chunk)
+        x = (rng.laplace(0.0, 1.0, size=(t1 - t0, k)) * s).astype(np.float32)
+        out[t0:t1] = x if dtype == F32 else _to_bf16_bits(x)
+    return out
+
+
+# Calibration batches: (name, tokens, channels, seed).  "calib_128x2048" stands in for
+# the pages' 128-sample calibration set (128 sequences of 2048 tokens) at the hidden
+# size of Llama3-8B; "calib_small" is a quick case for parity tests.
+CALIB = {
+    "calib_128x2048": (128 * 2048, 4096, 131),
+    "calib_small": (1000, 4096, 132),
+}
+
+
+def make_activations(name: str, tokens: Optional[int] = None) -> np.ndarray:
+    """Seeded bf16 activations [T, K] (uint16 bits) for the E|x| reduction: the profile
+    is drawn first, then the tokens, from one PCG64 stream."""
+    T, k, seed = CALIB[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    profile = draw_act(rng, k)
+    return draw_activations(rng, T if tokens is None else tokens, profile, BF16)
+
+
 def random_matrix(n: int, k: int, dtype: int, seed: int) -> Matrix:
     """Small ad-hoc matrices for edge-case tests (same distributions)."""
     return make_matrix(f"rand{n}x{k}", n, k, dtype, seed)
