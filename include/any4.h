@@ -153,6 +153,43 @@ int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8
 int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_final,
                     int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- bookends: the calibration statistic the quantizer consumes and the
+ * dequantization of what it emits. ---- */
+
+/* Workspace for any4_act_absmean: fp64 partial sums over token slices (the slice
+ * plan depends only on n_tokens and n_cols).  Returns ANY4_ERR_INVALID_ARG for a
+ * NULL bytes_out, n_tokens < 1 or n_cols < 1. */
+int any4_act_absmean_workspace_bytes(int64_t n_tokens, int64_t n_cols, size_t* bytes_out);
+
+/* E|x_j|, the mean absolute activation of each input channel over a calibration batch
+ * (Section 4.1; the sample weights of Eq. 23 are alpha_{i,j} * E|x_j|):
+ *   act_absmean[j] = fp32( (sum over t of |x[t, j]|, in fp64) / n_tokens ).
+ *   x            [n_tokens, n_cols] row-major activations, fp32 or bf16 bits (x_dtype)
+ *   act_absmean  out [n_cols] fp32, ready to pass to any4_quantize
+ *   workspace    device, >= any4_act_absmean_workspace_bytes(n_tokens, n_cols)
+ * The fp64 sums are taken over fixed token slices and added in slice order, so the
+ * result is deterministic; against a sequential fp64 sum it can differ only through
+ * the rounding of that sum, i.e. by at most one fp32 ulp.  Inf and NaN inputs
+ * propagate to their channel.  Errors: ANY4_ERR_INVALID_ARG (NULL pointer, n_tokens
+ * or n_cols < 1, bad dtype), ANY4_ERR_WORKSPACE, ANY4_ERR_HIP. */
+int any4_act_absmean(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t n_cols,
+                     float* act_absmean, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Dequantization (Section 2.5.2, Eq. 4: dequant(w_Q) = alpha * w_Q + beta, w_Q the
+ * row's LUT entry at the element's code):
+ *   w_out[i, j] = fl(fl(alpha_{i,g(j)} * LUT_i[q_ij]) + beta_{i,g(j)})
+ * evaluated in fp32 from the fp16 LUT, scale and offset (product and sum rounded
+ * separately), written as fp32 (out_dtype ANY4_F32) or as bf16 rounded to nearest
+ * even (ANY4_BF16).  Reads the codes, lut, scale and offset fields of `m` (its w,
+ * act_absmean and objective are not used); params->group and params->n_clusters must
+ * be the ones the codes were made with (iters and seed are ignored).  A code at or
+ * above n_clusters gives NaN.  w_out is [n_rows, n_cols], caller-allocated.
+ * Errors: ANY4_ERR_INVALID_ARG (NULL pointer, odd n_cols, group not dividing n_cols,
+ * bad n_clusters or out_dtype), ANY4_ERR_HIP. */
+int any4_dequantize(const any4_matrix* m, const any4_params* params, void* w_out,
+                    int32_t out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

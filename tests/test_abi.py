@@ -123,6 +123,31 @@ def test_quantize_rejects_before_launch(L):
     assert L.any4_stage_full(ctypes.byref(m), ctypes.byref(p), None, None, None, 0, None) == 3
 
 
+def test_bookends_validate_before_launch(L):
+    """E|x| and dequantization reject bad arguments synchronously (no HIP call)."""
+    n = ctypes.c_size_t(0)
+    assert L.any4_act_absmean_workspace_bytes(1000, 4096, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.any4_act_absmean_workspace_bytes(0, 4096, ctypes.byref(n)) == 1
+    assert L.any4_act_absmean_workspace_bytes(10, 0, ctypes.byref(n)) == 1
+    assert L.any4_act_absmean_workspace_bytes(10, 8, None) == 1
+    L.any4_act_absmean_workspace_bytes(262144, 4096, ctypes.byref(n))
+    assert n.value <= 64 << 20           # fp64 partials stay small next to the batch
+    assert L.any4_act_absmean(0x7000, 1, 10, 8, 0x8000, None, 0, None) == 3
+    assert L.any4_act_absmean(None, 1, 10, 8, 0x8000, 0x9000, 1 << 20, None) == 1
+    assert L.any4_act_absmean(0x7000, 3, 10, 8, 0x8000, 0x9000, 1 << 20, None) == 1
+    assert L.any4_act_absmean(0x7000, 1, 0, 8, 0x8000, 0x9000, 1 << 20, None) == 1
+    p = any4.params(128, 16, 20, 0)
+    m = _mat()
+    assert L.any4_dequantize(ctypes.byref(m), ctypes.byref(p), None, 1, None) == 1
+    assert L.any4_dequantize(ctypes.byref(m), ctypes.byref(p), 0x7000, 5, None) == 1
+    assert L.any4_dequantize(ctypes.byref(m), ctypes.byref(any4.params(96)), 0x7000, 1, None) == 1
+    assert L.any4_dequantize(ctypes.byref(_mat(k=500)), ctypes.byref(p), 0x7000, 1, None) == 1
+    assert L.any4_dequantize(None, ctypes.byref(p), 0x7000, 1, None) == 1
+    m0 = any4.Any4Matrix()
+    m0.n_rows, m0.n_cols = 0, 256
+    assert L.any4_dequantize(ctypes.byref(m0), ctypes.byref(p), None, 1, None) == 0
+
+
 def test_launch_geometry(L):
     assert any4.launch_geometry(4096) == (32, 2)
     assert any4.launch_geometry(512) == (8, 1)

@@ -25,6 +25,7 @@ EXPORTED = [
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
     "any4_stage_full",
+    "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize",
 ]
 
 
@@ -84,6 +85,11 @@ def lib():
         L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
         L.any4_launch_geometry.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
+        L.any4_act_absmean_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+        L.any4_act_absmean.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P,
+                                       ctypes.c_size_t, P]
+        L.any4_dequantize.argtypes = [MP, PP, P, ctypes.c_int32, P]
         for name in EXPORTED:
             if name != "any4_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -237,6 +243,56 @@ def quantize(w, act, group: int = 128, n_clusters: int = 16, iters: int = 20, se
 
 def read_status(ws) -> int:
     return lib().any4_read_device_status(_ptr(ws), _stream(ws.device))
+
+
+# ---------------------------------------------------------------------------------
+# bookends: E|x| of a calibration batch, and dequantization of the emitted codes
+
+def act_absmean_workspace_bytes(n_tokens: int, n_cols: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().any4_act_absmean_workspace_bytes(n_tokens, n_cols, ctypes.byref(n)),
+           "any4_act_absmean_workspace_bytes")
+    return n.value
+
+
+def act_absmean(x, out=None, ws=None):
+    """E|x_j| [K] fp32 of activations x [T, K] (bf16 or fp32) on the GPU."""
+    torch = _torch()
+    _require_gpu(x)
+    code, x = _dtype_code(x)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [T, K] tensor")
+    T, K = int(x.shape[0]), int(x.shape[1])
+    if out is None:
+        out = torch.empty((K,), dtype=torch.float32, device=x.device)
+    need = act_absmean_workspace_bytes(T, K)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check(lib().any4_act_absmean(_ptr(x), code, T, K, _ptr(out), _ptr(ws), ws.numel(),
+                                  _stream(x.device)), "any4_act_absmean")
+    return out
+
+
+def dequantize(q: Quantized, group: int = 128, n_clusters: int = 16, out_dtype=None, out=None):
+    """Eq. 4 dequantization alpha * LUT[q] + beta of a quantized matrix to [N, K]
+    bf16 (default) or fp32."""
+    torch = _torch()
+    _require_gpu(q.codes)
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    N, K = int(q.codes.shape[0]), int(q.codes.shape[1]) * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=q.codes.device)
+    m = Any4Matrix()
+    m.n_rows, m.n_cols = N, K
+    m.w_dtype = ANY4_F32
+    m.codes, m.lut, m.scale, m.offset = _ptr(q.codes), _ptr(q.lut), _ptr(q.scale), _ptr(q.offset)
+    p = params(group, n_clusters, 0, 0)
+    code = ANY4_BF16 if out_dtype == torch.bfloat16 else ANY4_F32
+    _check(lib().any4_dequantize(ctypes.byref(m), ctypes.byref(p), _ptr(out), code,
+                                 _stream(q.codes.device)), "any4_dequantize")
+    return out
 
 
 # ---------------------------------------------------------------------------------

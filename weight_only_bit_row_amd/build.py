@@ -24,7 +24,7 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-SOURCES = ["any4_kernels.hip", "any4_api.cpp"]
+SOURCES = ["any4_kernels.hip", "any4_bookends.hip", "any4_api.cpp"]
 
 
 def build(verbose: bool = False) -> str:

@@ -249,4 +249,51 @@ int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_fi
   return launch_one(make_args(params, 1, status), d, any4::MODE_FULL, stream);
 }
 
+int any4_act_absmean_workspace_bytes(int64_t n_tokens, int64_t n_cols, size_t* bytes_out) {
+  if (!bytes_out || n_tokens < 1 || n_cols < 1) return ANY4_ERR_INVALID_ARG;
+  *bytes_out = any4::plan_absmean(n_tokens, n_cols).partial_bytes;
+  return ANY4_OK;
+}
+
+int any4_act_absmean(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t n_cols,
+                     float* act_absmean, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (!x || !act_absmean || n_tokens < 1 || n_cols < 1) return ANY4_ERR_INVALID_ARG;
+  if (x_dtype != ANY4_F32 && x_dtype != ANY4_BF16) return ANY4_ERR_INVALID_ARG;
+  const any4::AbsmeanPlan plan = any4::plan_absmean(n_tokens, n_cols);
+  if (!workspace || workspace_bytes < plan.partial_bytes) return ANY4_ERR_WORKSPACE;
+  return any4::launch_absmean(x, x_dtype, n_tokens, n_cols, act_absmean,
+                              static_cast<double*>(workspace), plan, stream) == hipSuccess
+             ? ANY4_OK
+             : ANY4_ERR_HIP;
+}
+
+int any4_dequantize(const any4_matrix* m, const any4_params* params, void* w_out,
+                    int32_t out_dtype, hipStream_t stream) {
+  if (!m || !params) return ANY4_ERR_INVALID_ARG;
+  if (params->group < 2 || !is_pow2(params->group)) return ANY4_ERR_INVALID_ARG;
+  if (!(params->n_clusters == 2 || params->n_clusters == 4 || params->n_clusters == 8 ||
+        params->n_clusters == 16))
+    return ANY4_ERR_INVALID_ARG;
+  if (m->n_rows < 0 || m->n_cols < 2 || (m->n_cols & 1) || m->n_cols % params->group != 0)
+    return ANY4_ERR_INVALID_ARG;
+  if (out_dtype != ANY4_F32 && out_dtype != ANY4_BF16) return ANY4_ERR_INVALID_ARG;
+  if (m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows == 0) return ANY4_OK;
+  if (!m->codes || !m->lut || !m->scale || !m->offset || !w_out) return ANY4_ERR_INVALID_ARG;
+  any4::DequantDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.codes = m->codes;
+  d.lut = m->lut;
+  d.scale = m->scale;
+  d.offset = m->offset;
+  d.out = w_out;
+  d.n_rows = m->n_rows;
+  d.n_cols = m->n_cols;
+  d.group = params->group;
+  d.n_clusters = params->n_clusters;
+  d.out_bf16 = out_dtype == ANY4_BF16 ? 1 : 0;
+  return any4::launch_dequant(d, stream) == hipSuccess ? ANY4_OK : ANY4_ERR_HIP;
+}
+
 }  // extern "C"

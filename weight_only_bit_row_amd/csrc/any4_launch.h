@@ -67,4 +67,32 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_t* assign,
                        const float* c, const float* alpha, const float* beta, hipStream_t stream);
 
+// ---- bookends (any4_bookends.hip)
+
+// E|x_j| reduction: token slices of the [T, K] batch and the fp64 partial sums they need.
+struct AbsmeanPlan {
+  int64_t n_splits;          // token slices, each summed on its own
+  int64_t tokens_per_split;
+  size_t partial_bytes;      // n_splits * K fp64 partial sums
+};
+AbsmeanPlan plan_absmean(int64_t n_tokens, int64_t n_cols);
+hipError_t launch_absmean(const void* x, int dtype, int64_t n_tokens, int64_t n_cols, float* out,
+                          double* partial, const AbsmeanPlan& plan, hipStream_t stream);
+
+// Eq. 4 dequantization of one matrix's emitted codes/LUT/scale/offset.
+struct DequantDesc {
+  const uint8_t* codes;
+  const uint16_t* lut;
+  const uint16_t* scale;
+  const uint16_t* offset;
+  void* out;
+  int64_t n_rows;
+  int64_t n_cols;
+  int32_t group;
+  int32_t n_clusters;
+  int32_t out_bf16;          // 0: fp32 output, 1: bf16 (round to nearest even)
+  int32_t pad_;
+};
+hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream);
+
 }  // namespace any4
