@@ -9,6 +9,11 @@ outputs are preallocated.  Prints ONE JSON line.
   python bench.py --profile-steps 3          # short run for rocprofv3
   python bench.py --profile-steps 2 --iters 0   # same, without Lloyd rounds (counter deltas)
   python bench.py --copy-calibration         # plain copy of known size (counter scale)
+  python bench.py --bookends-only --profile-steps 5   # only E|x| and dequantization
+
+The same line reports the two bookend kernels (E|x| of a calibration batch and the
+Eq. 4 dequantization of the quantized matrix) against the HBM roofline under
+"bookends"; they run after the timed quantizer steps and are not part of `value`.
 """
 from __future__ import annotations
 
@@ -26,6 +31,9 @@ if ROOT not in sys.path:
 
 KERNEL_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "any4_rows_up_proj_counters.md")
+BOOKENDS_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_bookends.hip")
+BOOKENDS_COUNTERS = os.path.join(ROOT, "profiles", "any4_bookends_counters.md")
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed FMA counted as 2 flops x 2 lanes)
 METRIC = "Lloyd elem-iters/sec and % FP32 VALU peak; ms per 14336x4096 matrix"
@@ -38,19 +46,19 @@ def credited_flops_per_element(k: int, iters: int) -> int:
     return 6 + 4 * k + iters * (3 * k + 1) + (3 * k + 2)
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
+def load_traffic(counters: str = COUNTERS, src: str = KERNEL_SRC, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the
     current kernel source; otherwise None."""
-    if not os.path.exists(COUNTERS):
+    if not os.path.exists(counters):
         return None
-    text = open(COUNTERS).read()
+    text = open(counters).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    t = re.search(key + r":\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash(src):
         return None
     return float(t.group(1))
 
@@ -102,6 +110,68 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
+def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
+    """E|x| of a calibration batch and the Eq. 4 dequantization of the quantized matrix,
+    each timed over a batch of launches with HIP events on the launch stream."""
+    from workloads import CALIB, make_activations
+
+    x_np = make_activations("calib_32x2048")
+    T, Kx = x_np.shape
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    del x_np
+    act_out = torch.empty((Kx,), dtype=torch.float32, device=dev)
+    ws = torch.empty((any4.act_absmean_workspace_bytes(T, Kx),), dtype=torch.uint8, device=dev)
+    w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+
+    def run_abs():
+        any4.act_absmean(x, out=act_out, ws=ws)
+
+    def run_dq():
+        any4.dequantize(q, g, k, out=w_hat)
+
+    if profile_steps:
+        for _ in range(profile_steps):
+            run_abs()
+            run_dq()
+        torch.cuda.synchronize()
+        return None
+
+    def per_launch_ms(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_abs = per_launch_ms(run_abs, 20)
+    ms_dq = per_launch_ms(run_dq, 100)
+    bytes_abs = T * Kx * 2 + Kx * 4                      # read x once, write E|x|
+    bytes_dq = N * K // 2 + N * k * 2 + 2 * N * (K // g) * 2 + N * K * 2   # codes, LUT, alpha/beta; bf16 out
+
+    def roof(nbytes, ms, key):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS,
+                "traffic": load_traffic(BOOKENDS_COUNTERS, BOOKENDS_SRC, key),
+                "algorithmic_bytes": nbytes}
+
+    return [
+        {"kernel": "any4_act_absmean (absmean_partial_kernel + absmean_finish_kernel)",
+         "workload": f"E|x| of {T} calibration tokens x {Kx} channels, bf16 "
+                     f"(32 sequences of 2048 tokens, seed {CALIB['calib_32x2048'][2]})",
+         "ms_per_call": ms_abs, "roofline": roof(bytes_abs, ms_abs, "absmean_traffic_bytes_per_launch")},
+        {"kernel": "any4_dequantize (dequant_vec_kernel, bf16 out)",
+         "workload": f"Eq. 4 dequantization of the quantized {N}x{K} up_proj (group {g}, "
+                     f"{k} clusters) to bf16",
+         "ms_per_call": ms_dq, "roofline": roof(bytes_dq, ms_dq, "dequant_traffic_bytes_per_launch")},
+    ]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +183,9 @@ def main():
                     help="Lloyd rounds for --profile-steps runs (default: the workload's 20)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bookends", action="store_true", help="skip the E|x| and dequant kernels")
+    ap.add_argument("--bookends-only", action="store_true",
+                    help="with --profile-steps: run only the E|x| and dequant kernels")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -139,6 +212,12 @@ def main():
     out = any4.quantize(w, act, group=g, n_clusters=k, iters=iters)   # allocates outputs
     ws = any4.workspace(dev)
     torch.cuda.synchronize()
+
+    if args.profile_steps and args.bookends_only:
+        bookends(any4, torch, np, out, N, K, g, k, dev, torch.cuda.current_stream(dev),
+                 profile_steps=args.profile_steps)
+        print(json.dumps({"profile_steps": args.profile_steps, "bookends_only": True}))
+        return
 
     if args.profile_steps:
         p_iters = iters if args.iters is None else args.iters
@@ -212,6 +291,8 @@ def main():
             "kernel_ms_mean_hip_events": ms_kernel,
         },
     }
+    if not args.no_bookends:
+        line["bookends"] = bookends(any4, torch, np, out, N, K, g, k, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(m, g, k, iters)
     print(json.dumps(line))

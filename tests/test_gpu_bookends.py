@@ -206,3 +206,33 @@ def test_output_error_any4_below_int4_end_to_end():
     e4, ei = rel(w_any4), rel(w_int4)
     say(f"  output error: any4 {e4:.4f}, int4 {ei:.4f}")
     assert e4 < ei
+
+
+# --- the sizes bench.py times, on sampled outputs -------------------------------------------
+
+def test_absmean_bench_batch_sampled_channels():
+    """E|x| of the 65536-token x 4096-channel calibration batch (the launch bench.py
+    times), checked on 96 sampled channels."""
+    x = make_activations("calib_32x2048")
+    say(f"absmean calib_32x2048: T={x.shape[0]} K={x.shape[1]}")
+    got = any4().act_absmean(_dev(x)).cpu().numpy()
+    cols = np.sort(np.random.default_rng(7).choice(x.shape[1], 96, replace=False))
+    ref = oracle.act_absmean(np.ascontiguousarray(x[:, cols]), BF16)
+    d = _ulp_diff(got[cols], ref)
+    say(f"  {np.mean(d == 0):.4f} of sampled channels bit-exact, max {d.max()} ulp")
+    assert d.max() <= 1
+
+
+def test_dequant_full_up_proj_sampled_rows():
+    """Dequantization of the whole quantized 14336 x 4096 up_proj to bf16 (the launch
+    bench.py times), checked on 64 sampled rows."""
+    w = make("up_proj")
+    m = w.matrices[0]
+    wd, act = to_device(m)
+    q = any4().quantize(wd, act, w.group, w.n_clusters, w.iters)
+    out = any4().dequantize(q, w.group, w.n_clusters).cpu().view(torch.int16).numpy().view(np.uint16)
+    rows = np.sort(np.random.default_rng(8).choice(m.w.shape[0], 64, replace=False))
+    ref = oracle.dequantize(q.codes.cpu().numpy()[rows], q.lut.cpu().numpy()[rows].view(np.uint16),
+                            q.scale.cpu().numpy()[rows].view(np.uint16),
+                            q.offset.cpu().numpy()[rows].view(np.uint16), w.group, w.n_clusters)
+    assert np.array_equal(out[rows], oracle.bf16_bits(ref))

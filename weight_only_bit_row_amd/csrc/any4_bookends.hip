@@ -20,14 +20,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte vectors
 typedef float f32x4 __attribute__((ext_vector_type(4)));      // streaming loads and stores
 
 // ---------------------------------------------------------------------------------
-// E|x_j|.  Pass 1: block (cx, s) sums |x| over token slice s for 2048 consecutive
-// channels, 8 per lane, in fp64 and in token order.  Pass 2: channel j sums the
-// slices' partial sums in slice order, divides by T in fp64 and rounds to fp32.  The
-// slice plan depends only on (T, K), so results are the same on every launch.
+// E|x_j|.  Pass 1: workgroup (cx, s) covers 512 consecutive channels, 8 per lane, and
+// token slice s; its four waves take every fourth token of the slice (wave w: tokens
+// t0 + w, t0 + w + 4, ...), each summing |x| in fp64 in token order, and the four sums
+// are added in wave order through LDS.  Pass 2: each channel's slice sums are added in
+// slice order by four waves (a quarter of the slices each, combined in wave order),
+// divided by T in fp64 and rounded to fp32.  The plan depends only on (T, K), so
+// results are the same on every launch.
 
 constexpr int kAbsChannels = 8;   // per lane: one 16-byte load of bf16, two of fp32
-constexpr int kAbsUnroll = 8;     // tokens whose loads are in flight together
-constexpr int64_t kAbsBlockChannels = int64_t(kThreads) * kAbsChannels;
+constexpr int kAbsUnroll = 16;    // tokens whose loads are in flight together per wave
+constexpr int kAbsWaves = kThreads / 64;
+constexpr int64_t kAbsBlockChannels = int64_t(64) * kAbsChannels;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -55,74 +59,107 @@ __global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const void* _
                                                                    int64_t T, int64_t K,
                                                                    int64_t tokens_per_split,
                                                                    double* __restrict__ partial) {
-  const int64_t j0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * kAbsChannels;
-  if (j0 >= K) return;
+  __shared__ double red[kAbsWaves - 1][64][kAbsChannels];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j0 = (int64_t(blockIdx.x) * 64 + lane) * kAbsChannels;
   const int64_t s = blockIdx.y;
   const int64_t t0 = s * tokens_per_split;
   const int64_t t1 = (t0 + tokens_per_split < T) ? t0 + tokens_per_split : T;
   double acc[kAbsChannels];
 #pragma unroll
   for (int i = 0; i < kAbsChannels; ++i) acc[i] = 0.0;
-  if (VEC) {
-    // row t starts at element t*K; 16-byte vectors of this lane's channels
-    constexpr int kElem = BF16 ? 2 : 4;
-    const char* base = static_cast<const char*>(x) + j0 * kElem;
-    const int64_t row_bytes = K * kElem;
-    int64_t t = t0;
-    for (; t + kAbsUnroll <= t1; t += kAbsUnroll) {
-      u32x4 v[kAbsUnroll], v2[kAbsUnroll];
+  if (j0 < K) {
+    if (VEC) {
+      constexpr int kElem = BF16 ? 2 : 4;
+      const char* base = static_cast<const char*>(x) + j0 * kElem;
+      const int64_t row_bytes = K * kElem;
+      int64_t t = t0 + wave;
+      for (; t + int64_t(kAbsWaves) * (kAbsUnroll - 1) < t1; t += int64_t(kAbsWaves) * kAbsUnroll) {
+        u32x4 v[kAbsUnroll], v2[kAbsUnroll];
 #pragma unroll
-      for (int u = 0; u < kAbsUnroll; ++u) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(base + (t + u) * row_bytes);
-        v[u] = __builtin_nontemporal_load(p);
-        if (!BF16) v2[u] = __builtin_nontemporal_load(p + 1);
+        for (int u = 0; u < kAbsUnroll; ++u) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(base + (t + kAbsWaves * u) * row_bytes);
+          v[u] = __builtin_nontemporal_load(p);
+          if (!BF16) v2[u] = __builtin_nontemporal_load(p + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < kAbsUnroll; ++u) add_abs8(acc, v[u], BF16, BF16 ? v[u] : v2[u]);
       }
+      for (; t < t1; t += kAbsWaves) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(base + t * row_bytes);
+        const u32x4 v = __builtin_nontemporal_load(p);
+        const u32x4 v2 = BF16 ? v : __builtin_nontemporal_load(p + 1);
+        add_abs8(acc, v, BF16, v2);
+      }
+    } else {
+      for (int64_t t = t0 + wave; t < t1; t += kAbsWaves) {
 #pragma unroll
-      for (int u = 0; u < kAbsUnroll; ++u) add_abs8(acc, v[u], BF16, BF16 ? v[u] : v2[u]);
-    }
-    for (; t < t1; ++t) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(base + t * row_bytes);
-      const u32x4 v = __builtin_nontemporal_load(p);
-      const u32x4 v2 = BF16 ? v : __builtin_nontemporal_load(p + 1);
-      add_abs8(acc, v, BF16, v2);
-    }
-  } else {
-    for (int64_t t = t0; t < t1; ++t) {
-#pragma unroll
-      for (int i = 0; i < kAbsChannels; ++i) {
-        const int64_t j = j0 + i;
-        if (j < K) {
-          float f;
-          if (BF16)
-            f = __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[t * K + j]) << 16);
-          else
-            f = static_cast<const float*>(x)[t * K + j];
-          acc[i] += fabs(static_cast<double>(f));
+        for (int i = 0; i < kAbsChannels; ++i) {
+          const int64_t j = j0 + i;
+          if (j < K) {
+            float f;
+            if (BF16)
+              f = __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[t * K + j]) << 16);
+            else
+              f = static_cast<const float*>(x)[t * K + j];
+            acc[i] += fabs(static_cast<double>(f));
+          }
         }
       }
     }
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int i = 0; i < kAbsChannels; ++i)
-    if (j0 + i < K) partial[s * K + j0 + i] = acc[i];
+    for (int i = 0; i < kAbsChannels; ++i) red[wave - 1][lane][i] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && j0 < K) {
+#pragma unroll
+    for (int w = 0; w < kAbsWaves - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < kAbsChannels; ++i) acc[i] += red[w][lane][i];
+#pragma unroll
+    for (int i = 0; i < kAbsChannels; ++i)
+      if (j0 + i < K) partial[s * K + j0 + i] = acc[i];
+  }
 }
 
+// 64 channels per workgroup; wave w adds slices w, w + 4, ... in order, then wave 0
+// adds the four sums in wave order.
 __global__ __launch_bounds__(kThreads) void absmean_finish_kernel(const double* __restrict__ partial,
                                                                   int64_t n_splits, int64_t T,
                                                                   int64_t K, float* __restrict__ out) {
-  const int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (j >= K) return;
+  __shared__ double red[kAbsWaves - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = int64_t(blockIdx.x) * 64 + lane;
   double sum = 0.0;
-  for (int64_t s = 0; s < n_splits; ++s) sum += partial[s * K + j];
-  out[j] = static_cast<float>(sum / static_cast<double>(T));
+  if (j < K) {
+    int64_t s = wave;
+    for (; s + 3 * kAbsWaves < n_splits; s += 4 * kAbsWaves) {  // four loads in flight
+      const double p0 = partial[s * K + j], p1 = partial[(s + kAbsWaves) * K + j];
+      const double p2 = partial[(s + 2 * kAbsWaves) * K + j], p3 = partial[(s + 3 * kAbsWaves) * K + j];
+      sum += p0;
+      sum += p1;
+      sum += p2;
+      sum += p3;
+    }
+    for (; s < n_splits; s += kAbsWaves) sum += partial[s * K + j];
+  }
+  if (wave > 0) red[wave - 1][lane] = sum;
+  __syncthreads();
+  if (wave == 0 && j < K) {
+#pragma unroll
+    for (int w = 0; w < kAbsWaves - 1; ++w) sum += red[w][lane];
+    out[j] = static_cast<float>(sum / static_cast<double>(T));
+  }
 }
 
 // ---------------------------------------------------------------------------------
-// Dequantization.  One workgroup per row; the row's LUT is widened to fp32 in LDS
-// (entries beyond n_clusters hold NaN, so a code outside the LUT gives NaN).  In the
-// vector path each lane takes 16 consecutive columns: one 8-byte load of codes (the
-// 16 nibbles in column order, low nibble first), one alpha/beta pair when the group
-// spans them, and 64 (fp32) or 32 (bf16) bytes of 16-byte stores.
+// Dequantization.  A row's LUT is widened to fp32 in LDS (entries beyond n_clusters
+// hold NaN, so a code outside the LUT gives NaN).  In the vector path each lane takes
+// 16 consecutive columns at a time: one 8-byte load of codes (the 16 nibbles in column
+// order, low nibble first), one alpha/beta pair (the group spans the 16 columns), and
+// 64 (fp32) or 32 (bf16) bytes of 16-byte stores.
 
 constexpr int kDqCols = 16;
 
@@ -132,11 +169,12 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return static_cast<float>(v);  // exact widening
 }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// two floats -> two bfloat16 in one register (low half first), round to nearest even,
+// NaN stays NaN (gfx950 converts a pair in one instruction)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // w_hat = fl(fl(alpha * level) + beta): the kernels are built without contraction
@@ -145,8 +183,96 @@ __device__ __forceinline__ float dequant_one(float alpha, float level, float bet
   return prod + beta;
 }
 
-template <bool BF16_OUT, bool VEC>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const DequantDesc d) {
+__device__ __forceinline__ void dequant_store16(void* out, int64_t off, float alpha, float beta,
+                                                uint64_t nib, const float* lut, bool bf16_out) {
+  float w[kDqCols];
+#pragma unroll
+  for (int e = 0; e < kDqCols; ++e) w[e] = dequant_one(alpha, lut[(nib >> (4 * e)) & 0xF], beta);
+  if (bf16_out) {
+    uint32_t p[kDqCols / 2];
+#pragma unroll
+    for (int e = 0; e < kDqCols / 2; ++e) p[e] = bf16x2_rne_bits(w[2 * e], w[2 * e + 1]);
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off);
+    dst[0] = u32x4{p[0], p[1], p[2], p[3]};
+    dst[1] = u32x4{p[4], p[5], p[6], p[7]};
+  } else {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(out) + off);
+#pragma unroll
+    for (int v = 0; v < kDqCols / 4; ++v)
+      dst[v] = f32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
+  }
+}
+
+// Vector path (K % 16 == 0, group % 16 == 0, aligned pointers): a workgroup takes
+// kDqRows rows; chunk id = r * (K / 16) + c is columns [16c, 16c + 16) of row r, and
+// lane t takes ids t, t + 256, ...  The codes and scale/offset of a lane's first
+// kDqPre chunks are requested before the LUTs are staged, so their latency overlaps
+// the LUT loads and the barrier.
+constexpr int kDqRows = 4;
+constexpr int kDqPre = 4;
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kThreads) void dequant_vec_kernel(const DequantDesc d) {
+  __shared__ float lut[kDqRows][16];
+  const int tid = threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.x) * kDqRows;
+  const int nr = (d.n_rows - r0 < kDqRows) ? static_cast<int>(d.n_rows - r0) : kDqRows;
+  const int64_t K = d.n_cols, G = K / d.group;
+  const int cpr = static_cast<int>(K / kDqCols);   // chunks per row (K <= 2^31 columns)
+  // lane's chunk (row rr, chunk c) for id = tid, tid + 256, ...: step c by 256 and
+  // carry whole rows into rr
+  int rr = tid / cpr, c = tid - (tid / cpr) * cpr;
+  uint64_t nib[kDqPre];
+  uint16_t ab[kDqPre], bb[kDqPre];
+  int pr[kDqPre], pc[kDqPre];
+#pragma unroll
+  for (int p = 0; p < kDqPre; ++p) {
+    pr[p] = rr;
+    pc[p] = c;
+    nib[p] = 0;
+    ab[p] = bb[p] = 0;
+    if (rr < nr) {
+      const int64_t r = r0 + rr, c0 = int64_t(c) * kDqCols;
+      const uint2 cb = *reinterpret_cast<const uint2*>(d.codes + r * (K / 2) + c0 / 2);
+      nib[p] = (uint64_t(cb.y) << 32) | cb.x;
+      ab[p] = d.scale[r * G + c0 / d.group];
+      bb[p] = d.offset[r * G + c0 / d.group];
+    }
+    c += kThreads;
+    while (c >= cpr) {
+      c -= cpr;
+      ++rr;
+    }
+  }
+  if (tid < nr * 16) {
+    const int r = tid >> 4, e = tid & 15;
+    lut[r][e] = e < d.n_clusters ? half_bits_to_float(d.lut[(r0 + r) * d.n_clusters + e])
+                                 : __builtin_nanf("");
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kDqPre; ++p) {
+    if (pr[p] < nr)
+      dequant_store16(d.out, (r0 + pr[p]) * K + int64_t(pc[p]) * kDqCols, half_bits_to_float(ab[p]),
+                      half_bits_to_float(bb[p]), nib[p], lut[pr[p]], BF16_OUT);
+  }
+  for (; rr < nr;) {
+    const int64_t r = r0 + rr, c0 = int64_t(c) * kDqCols;
+    const uint2 cb = *reinterpret_cast<const uint2*>(d.codes + r * (K / 2) + c0 / 2);
+    const uint64_t nb = (uint64_t(cb.y) << 32) | cb.x;
+    dequant_store16(d.out, r * K + c0, half_bits_to_float(d.scale[r * G + c0 / d.group]),
+                    half_bits_to_float(d.offset[r * G + c0 / d.group]), nb, lut[rr], BF16_OUT);
+    c += kThreads;
+    while (c >= cpr) {
+      c -= cpr;
+      ++rr;
+    }
+  }
+}
+
+// Scalar path (any even K, any group): one workgroup per row, one column per lane step.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantDesc d) {
   __shared__ float lut[16];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -159,45 +285,15 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const DequantDesc d) 
   const uint8_t* codes = d.codes + row * (K / 2);
   const uint16_t* scale = d.scale + row * G;
   const uint16_t* offset = d.offset + row * G;
-  if (VEC) {
-    // K % 16 == 0, group % 16 == 0 and aligned pointers: 16 columns share one group
-    for (int64_t c0 = int64_t(tid) * kDqCols; c0 < K; c0 += int64_t(kThreads) * kDqCols) {
-      const uint2 cb = *reinterpret_cast<const uint2*>(codes + c0 / 2);
-      const uint64_t nib = (uint64_t(cb.y) << 32) | cb.x;
-      const int64_t g = c0 / d.group;
-      const float alpha = half_bits_to_float(scale[g]);
-      const float beta = half_bits_to_float(offset[g]);
-      float w[kDqCols];
-#pragma unroll
-      for (int e = 0; e < kDqCols; ++e)
-        w[e] = dequant_one(alpha, lut[(nib >> (4 * e)) & 0xF], beta);
-      if (BF16_OUT) {
-        uint32_t p[kDqCols / 2];
-#pragma unroll
-        for (int e = 0; e < kDqCols / 2; ++e)
-          p[e] = bf16_rne_bits(w[2 * e]) | (bf16_rne_bits(w[2 * e + 1]) << 16);
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(d.out) + row * K + c0);
-        __builtin_nontemporal_store(u32x4{p[0], p[1], p[2], p[3]}, dst);
-        __builtin_nontemporal_store(u32x4{p[4], p[5], p[6], p[7]}, dst + 1);
-      } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(d.out) + row * K + c0);
-#pragma unroll
-        for (int v = 0; v < kDqCols / 4; ++v)
-          __builtin_nontemporal_store(f32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]},
-                                      dst + v);
-      }
-    }
-  } else {
-    for (int64_t j = tid; j < K; j += kThreads) {
-      const uint8_t byte = codes[j / 2];
-      const int q = (j & 1) ? (byte >> 4) : (byte & 0xF);
-      const int64_t g = j / d.group;
-      const float w = dequant_one(half_bits_to_float(scale[g]), lut[q], half_bits_to_float(offset[g]));
-      if (BF16_OUT)
-        static_cast<uint16_t*>(d.out)[row * K + j] = static_cast<uint16_t>(bf16_rne_bits(w));
-      else
-        static_cast<float*>(d.out)[row * K + j] = w;
-    }
+  for (int64_t j = tid; j < K; j += kThreads) {
+    const uint8_t byte = codes[j / 2];
+    const int q = (j & 1) ? (byte >> 4) : (byte & 0xF);
+    const int64_t g = j / d.group;
+    const float w = dequant_one(half_bits_to_float(scale[g]), lut[q], half_bits_to_float(offset[g]));
+    if (BF16_OUT)
+      static_cast<uint16_t*>(d.out)[row * K + j] = static_cast<uint16_t>(bf16x2_rne_bits(w, 0.0f));
+    else
+      static_cast<float*>(d.out)[row * K + j] = w;
   }
 }
 
@@ -206,10 +302,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 }  // namespace
 
 AbsmeanPlan plan_absmean(int64_t n_tokens, int64_t n_cols) {
-  // about 1024 workgroups (4 per CU) and at least 64 tokens per slice
+  // about 1024 workgroups (4 per CU) and at least 256 tokens (64 per wave) per slice
   const int64_t col_blocks = (n_cols + kAbsBlockChannels - 1) / kAbsBlockChannels;
   int64_t splits = (1024 + col_blocks - 1) / col_blocks;
-  const int64_t max_splits = (n_tokens + 63) / 64;
+  const int64_t max_splits = (n_tokens + 255) / 256;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   if (splits > 65535) splits = 65535;
@@ -240,7 +336,7 @@ hipError_t launch_absmean(const void* x, int dtype, int64_t n_tokens, int64_t n_
                        n_tokens, n_cols, plan.tokens_per_split, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(absmean_finish_kernel, dim3(static_cast<uint32_t>((n_cols + kThreads - 1) / kThreads)),
+  hipLaunchKernelGGL(absmean_finish_kernel, dim3(static_cast<uint32_t>((n_cols + 63) / 64)),
                      dim3(kThreads), 0, stream, partial, plan.n_splits, n_tokens, n_cols, out);
   return hipGetLastError();
 }
@@ -249,15 +345,16 @@ hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
   const bool vec = d.n_cols % kDqCols == 0 && d.group % kDqCols == 0 && aligned(d.codes, 8) &&
                    aligned(d.out, 16);
-  const dim3 grid(static_cast<uint32_t>(d.n_rows));
+  const dim3 grid_vec(static_cast<uint32_t>((d.n_rows + kDqRows - 1) / kDqRows));
+  const dim3 grid_row(static_cast<uint32_t>(d.n_rows));
   if (d.out_bf16 && vec)
-    hipLaunchKernelGGL((dequant_kernel<true, true>), grid, dim3(kThreads), 0, stream, d);
+    hipLaunchKernelGGL((dequant_vec_kernel<true>), grid_vec, dim3(kThreads), 0, stream, d);
   else if (d.out_bf16)
-    hipLaunchKernelGGL((dequant_kernel<true, false>), grid, dim3(kThreads), 0, stream, d);
+    hipLaunchKernelGGL((dequant_scalar_kernel<true>), grid_row, dim3(kThreads), 0, stream, d);
   else if (vec)
-    hipLaunchKernelGGL((dequant_kernel<false, true>), grid, dim3(kThreads), 0, stream, d);
+    hipLaunchKernelGGL((dequant_vec_kernel<false>), grid_vec, dim3(kThreads), 0, stream, d);
   else
-    hipLaunchKernelGGL((dequant_kernel<false, false>), grid, dim3(kThreads), 0, stream, d);
+    hipLaunchKernelGGL((dequant_scalar_kernel<false>), grid_row, dim3(kThreads), 0, stream, d);
   return hipGetLastError();
 }
 

@@ -174,11 +174,12 @@ def draw_activations(rng: np.random.Generator, n_tokens: int, profile: np.ndarra
     return out
 
 
-# Calibration batches: (name, tokens, channels, seed).  "calib_128x2048" stands in for
-# the pages' 128-sample calibration set (128 sequences of 2048 tokens) at the hidden
-# size of Llama3-8B; "calib_small" is a quick case for parity tests.
+# Calibration batches: (name, tokens, channels, seed).  "calib_32x2048" stands in for a
+# multi-sample calibration set (the pages compare their single prompt with 128 samples)
+# at the hidden size of Llama3-8B: 32 sequences of 2048 tokens, 512 MiB of bf16, large
+# enough to stream from HBM; "calib_small" is a quick case for parity tests.
 CALIB = {
-    "calib_128x2048": (128 * 2048, 4096, 131),
+    "calib_32x2048": (32 * 2048, 4096, 131),
     "calib_small": (1000, 4096, 132),
 }
 
