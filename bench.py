@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 KERNEL_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "any4_rows_up_proj_counters.md")
 BOOKENDS_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_bookends.hip")
-BOOKENDS_COUNTERS = os.path.join(ROOT, "profiles", "any4_bookends_counters.md")
+BOOKENDS_COUNTERS = os.path.join(ROOT, "profiles", "any4_bookends_calib32x2048_up_proj.md")
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed FMA counted as 2 flops x 2 lanes)
