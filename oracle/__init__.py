@@ -56,6 +56,15 @@ def lib():
         L.oracle_any4_quantize.argtypes = [P, i32, i64, i64, P, i64, i32, i32, i32, i32, u64,
                                            P, P, P, P, P, P, P, P, P]
         L.oracle_any4_quantize.restype = ctypes.c_int
+        L.oracle_any4_quantize_v.argtypes = [P, i32, i64, i64, P, i64, i32, i32, i32, i32, u64, i32,
+                                             P, P, P, P, P, P, P, P, P]
+        L.oracle_any4_quantize_v.restype = ctypes.c_int
+        L.oracle_scale_row_mode.argtypes = [P, i64, i32, i32, i32, P, P, P]
+        L.oracle_scale_row_mode.restype = ctypes.c_int
+        L.oracle_weights_row_mode.argtypes = [P, P, i64, i32, i32, P]
+        L.oracle_weights_row_mode.restype = ctypes.c_int
+        L.oracle_seed_row_init.argtypes = [P, P, i64, i32, u64, u64, u32, i32, i32, ctypes.c_float, P, P]
+        L.oracle_seed_row_init.restype = ctypes.c_int
         L.oracle_fp16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_fp16_to_f32.restype = ctypes.c_float
         L.oracle_bf16_rne_array.argtypes = [P, P, i64]
@@ -142,30 +151,46 @@ def dequantize(codes, lut, scale, offset, group: int, n_clusters: int) -> np.nda
 
 # --- row-level steps -------------------------------------------------------------
 
-def scale_row(w, group: int, n_clusters: int):
+# variant word (the paper's ablations; 0 = defaults): bits 0-1 sample weights
+# (0 alpha*E|x|, 1 E|x|, 2 none), bits 2-3 initialization (0 k-means++, 1 random,
+# 2 uniform levels), bit 4 symmetric scaling, bits 8-15 restarts - 1
+WEIGHT_ALPHA_ACT, WEIGHT_ACT, WEIGHT_NONE = 0, 1, 2
+INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM = 0, 1 << 2, 2 << 2
+SYMMETRIC = 1 << 4
+
+
+def restarts(n: int) -> int:
+    return (n - 1) << 8
+
+
+def scale_row(w, group: int, n_clusters: int, symmetric: bool = False):
     w = _f32(w)
     K = w.size
     ws = np.zeros(K, np.float32)
     al = np.zeros(K // group, np.float32)
     be = np.zeros(K // group, np.float32)
-    bad = lib().oracle_scale_row(_p(w), K, group, n_clusters - 1, _p(ws), _p(al), _p(be))
+    bad = lib().oracle_scale_row_mode(_p(w), K, group, n_clusters - 1, int(symmetric), _p(ws),
+                                      _p(al), _p(be))
     return ws, al, be, bool(bad)
 
 
-def weights_row(alpha, act, group: int):
+def weights_row(alpha, act, group: int, weighting: int = 0):
     alpha = _f32(alpha)
     act = _f32(act)
     a = np.zeros(act.size, np.float32)
-    bad = lib().oracle_weights_row(_p(alpha), _p(act), act.size, group, _p(a))
+    bad = lib().oracle_weights_row_mode(_p(alpha), _p(act), act.size, group, weighting, _p(a))
     return a, bool(bad)
 
 
-def seed_row(ws, a, n_clusters: int, seed: int = 0, row_id: int = 0, matrix_index: int = 0):
+def seed_row(ws, a, n_clusters: int, seed: int = 0, row_id: int = 0, matrix_index: int = 0,
+             init: int = 0, restart: int = 0, level0: float = 0.0):
+    """Initial centres; init 0 k-means++, 1 random, 2 uniform levels (plain codes, not
+    the shifted variant bits)."""
     ws, a = _f32(ws), _f32(a)
     c0 = np.zeros(n_clusters, np.float32)
     picks = np.zeros(n_clusters, np.int32)
-    lib().oracle_seed_row(_p(ws), _p(a), ws.size, n_clusters, seed, row_id, matrix_index,
-                          _p(c0), _p(picks))
+    lib().oracle_seed_row_init(_p(ws), _p(a), ws.size, n_clusters, seed, row_id, matrix_index,
+                               init, restart, level0, _p(c0), _p(picks))
     return c0, picks
 
 
@@ -214,7 +239,7 @@ def lloyd_row(ws, a, c0, iters: int):
 
 def quantize(w: np.ndarray, dtype: int, act: np.ndarray, group: int, n_clusters: int,
              iters: int, seed: int = 0, row_offset: int = 0, matrix_index: int = 0,
-             trace: bool = False) -> dict:
+             trace: bool = False, variant: int = 0) -> dict:
     """Run the oracle over all rows of ``w`` ([N, K]; float32, or uint16 bf16 bits)."""
     w = np.ascontiguousarray(w)
     assert w.dtype == (np.float32 if dtype == 0 else np.uint16)
@@ -233,8 +258,8 @@ def quantize(w: np.ndarray, dtype: int, act: np.ndarray, group: int, n_clusters:
     if trace:
         out["c_trace"] = np.zeros((N, iters + 1, n_clusters), np.float32)
         out["j_trace"] = np.zeros((N, iters + 1), np.float64)
-    st = lib().oracle_any4_quantize(
-        _p(w), dtype, N, K, _p(act), row_offset, matrix_index, group, n_clusters, iters, seed,
+    st = lib().oracle_any4_quantize_v(
+        _p(w), dtype, N, K, _p(act), row_offset, matrix_index, group, n_clusters, iters, seed, variant,
         _p(out["codes"]), _p(out["lut"]), _p(out["scale"]), _p(out["offset"]),
         _p(out["objective"]), _p(out.get("c_trace")), _p(out.get("j_trace")),
         _p(out["picks"]), _p(out["c_final"]))

@@ -21,7 +21,8 @@
  * scikit-learn Lloyd, numpy Philox4x64, numpy float16 casts, the storage cost
  * printed in Section 2.4.1; for the bookends E|x| and Eq. 4 dequantization, exact
  * rational means, a worked example, exact reconstruction of exact-level rows and
- * torch's bfloat16 cast).  Philox4x32-10's round constants are pinned only
+ * torch's bfloat16 cast; for the method variants, exact invariances, nearest-level
+ * codes, draw frequencies and restart minima).  Philox4x32-10's round constants are pinned only
  * through the shared round structure (Philox4x64-10 vs numpy) and a uniformity
  * test: its absolute stream is "parity unpinned".
  */
@@ -147,22 +148,33 @@ static float bf16_to_f32(uint16_t b) {
  * alpha = (max - min) / (Qmax - Qmin) with Qmax - Qmin = 2^n - 1, beta = min,
  * w_S = (w - beta) / alpha.  A constant group (alpha = 0) gets w_S = 0.
  * Returns 0, or 1 when a value or alpha is not finite. */
-int oracle_scale_row(const float* w, int64_t K, int32_t group, int32_t qr,
-                     float* ws, float* alpha, float* beta) {
+int oracle_scale_row_mode(const float* w, int64_t K, int32_t group, int32_t qr, int32_t symmetric,
+                          float* ws, float* alpha, float* beta) {
     int bad = 0;
     for (int64_t t = 0; t < K / group; ++t) {
         const float* wg = w + t * group;
-        float mn = wg[0], mx = wg[0];
+        float mn = wg[0], mx = wg[0], amax = 0.0f;
         for (int64_t j = 0; j < group; ++j) {
             if (!isfinite(wg[j])) bad = 1;
             if (wg[j] < mn) mn = wg[j];
             if (wg[j] > mx) mx = wg[j];
+            if (fabsf(wg[j]) > amax) amax = fabsf(wg[j]);
         }
-        float range = mx - mn;
-        float al = range / (float)qr;
+        float al, be;
+        if (symmetric) {
+            /* Eq. 3: alpha = max|w| / Qmax, beta = 0, with Qmax = 2^(n-1) (the int4 span
+             * -7..+8 of Section 2.5.1 has Qmax = 8), so w_S lies in [-Qmax, Qmax] */
+            al = amax / (float)((qr + 1) / 2);
+            be = 0.0f;
+        } else {
+            float range = mx - mn;
+            al = range / (float)qr;
+            be = mn;
+        }
         if (!isfinite(al)) bad = 1;
         alpha[t] = al;
-        beta[t] = mn;
+        beta[t] = be;
+        mn = be;
         for (int64_t j = 0; j < group; ++j) {
             if (al > 0.0f) {
                 float diff = wg[j] - mn;
@@ -175,17 +187,34 @@ int oracle_scale_row(const float* w, int64_t K, int32_t group, int32_t qr,
     return bad;
 }
 
+int oracle_scale_row(const float* w, int64_t K, int32_t group, int32_t qr,
+                     float* ws, float* alpha, float* beta) {
+    return oracle_scale_row_mode(w, K, group, qr, 0, ws, alpha, beta);
+}
+
 /* Step 2: the per-element sample weight of Eq. 23, alpha_{i,j} * E|x_j|, in fp32.
  * Returns 1 when an activation statistic is negative or not finite, or a weight
  * is not finite or above the bound. */
-int oracle_weights_row(const float* alpha, const float* act, int64_t K, int32_t group, float* a) {
+int oracle_weights_row_mode(const float* alpha, const float* act, int64_t K, int32_t group,
+                            int32_t weighting, float* a) {
     int bad = 0;
     for (int64_t j = 0; j < K; ++j) {
         if (!isfinite(act[j]) || act[j] < 0.0f) bad = 1;
-        a[j] = alpha[j / group] * act[j];
+        if (weighting == 0)
+            a[j] = alpha[j / group] * act[j];
+        else if (weighting == 1)
+            a[j] = act[j];
+        else
+            a[j] = 1.0f;
         if (!isfinite(a[j]) || a[j] > ORACLE_A_MAX) bad = 1;
     }
     return bad;
+}
+
+/* The minimization terms of Appendix C.1 (Table A3): weighting 0 is Eq. 23's
+ * alpha * E|x| (the default), 1 uses E|x| alone, 2 the plain scaled weights (a = 1). */
+int oracle_weights_row(const float* alpha, const float* act, int64_t K, int32_t group, float* a) {
+    return oracle_weights_row_mode(alpha, act, K, group, 0, a);
 }
 
 static float sqdist(float x, float c) {
@@ -205,9 +234,27 @@ static float sqdist(float x, float c) {
  * hi32(row)) and key (lo32(seed), hi32(seed)); r = floor(u * Q / 2^64); the pick is
  * the smallest j whose prefix sum of q exceeds r.  When every p_j is 0 the centre
  * is copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1. */
-int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
-                    uint64_t seed, uint64_t row_id, uint32_t matrix_index,
-                    float* c0, int32_t* picks) {
+/* Initial centres for the initializations of Appendix C.2 (Table A4):
+ *   init 0  k-means++ as described above;
+ *   init 1  random: k distinct elements drawn one after another, each with probability
+ *           proportional to a_j among the elements not yet drawn (scikit-learn's random
+ *           init with sample weights), with the same integer sampling and Philox draws;
+ *   init 2  uniform: the integer levels, c_t = level0 + t (int4's -7..8 up to the
+ *           translation of the scaled domain: level0 = 0 for asymmetric scaling,
+ *           1 - k/2 for symmetric); no draws, picks = -1.
+ * `restart` selects an independent draw stream for restarts: the Philox counter's
+ * second word is t + 16 * restart. */
+int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
+                         uint64_t seed, uint64_t row_id, uint32_t matrix_index,
+                         int32_t init, int32_t restart, float level0,
+                         float* c0, int32_t* picks) {
+    if (init == 2) {
+        for (int32_t t = 0; t < k; ++t) {
+            c0[t] = level0 + (float)t;
+            picks[t] = -1;
+        }
+        return ORACLE_OK;
+    }
     float* D = (float*)malloc((size_t)K * sizeof(float));
     float* p = (float*)malloc((size_t)K * sizeof(float));
     uint64_t* q = (uint64_t*)malloc((size_t)K * sizeof(uint64_t));
@@ -216,7 +263,10 @@ int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
     for (int32_t t = 0; t < k; ++t) {
         float M = 0.0f;
         for (int64_t j = 0; j < K; ++j) {
-            p[j] = (t == 0) ? a[j] : a[j] * D[j];
+            if (init == 1)
+                p[j] = (t == 0) ? a[j] : p[j];    /* drawn elements were set to 0 below */
+            else
+                p[j] = (t == 0) ? a[j] : a[j] * D[j];
             if (p[j] > M) M = p[j];
         }
         if (M == 0.0f) {
@@ -232,7 +282,7 @@ int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
                 q[j] = (uint64_t)floor(v);
                 Q += q[j];
             }
-            uint32_t ctr[4] = {(uint32_t)row_id, (uint32_t)t, matrix_index,
+            uint32_t ctr[4] = {(uint32_t)row_id, (uint32_t)(t + 16 * restart), matrix_index,
                                (uint32_t)(row_id >> 32)};
             uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
             uint32_t x[4];
@@ -247,14 +297,23 @@ int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
             }
             c0[t] = ws[pick];
             picks[t] = (int32_t)pick;
+            if (init == 1) p[pick] = 0.0f;
         }
-        for (int64_t j = 0; j < K; ++j) {
-            float d = sqdist(ws[j], c0[t]);
-            if (t == 0 || d < D[j]) D[j] = d;
+        if (init != 1) {
+            for (int64_t j = 0; j < K; ++j) {
+                float d = sqdist(ws[j], c0[t]);
+                if (t == 0 || d < D[j]) D[j] = d;
+            }
         }
     }
     free(D); free(p); free(q);
     return ORACLE_OK;
+}
+
+int oracle_seed_row(const float* ws, const float* a, int64_t K, int32_t k,
+                    uint64_t seed, uint64_t row_id, uint32_t matrix_index,
+                    float* c0, int32_t* picks) {
+    return oracle_seed_row_init(ws, a, K, k, seed, row_id, matrix_index, 0, 0, 0.0f, c0, picks);
 }
 
 /* Step 4a: E-step, Section 4.1 Eq. 18: each scaled weight goes to the LUT value
@@ -307,30 +366,46 @@ void oracle_pack_row(const uint8_t* q, int64_t K, uint8_t* codes) {
 /* ------------------------------------------------------------------------- */
 /* The whole path for rows [0, n_rows) of one matrix, row-major.
  * Per row (Algorithm 1 of the paper's Appendix A, minus the calibration and the
- * module loop): scale, weights, k-means++ seed, `iters` rounds of E-step then
+ * module loop): scale, weights, initial centres, `iters` rounds of E-step then
  * M-step, a final E-step, then emission (fp16 LUT in draw order, fp16 alpha and
- * beta, nibble-packed codes).  Traces are optional (NULL to skip):
+ * beta, nibble-packed codes).
+ *
+ * `variant` selects the method variants of the paper's ablations (0 = the defaults):
+ *   bits 0-1   sample weights (Appendix C.1): 0 alpha*E|x|, 1 E|x|, 2 none (a = 1)
+ *   bits 2-3   initialization (Appendix C.2): 0 k-means++, 1 random, 2 uniform levels
+ *   bit 4      symmetric scaling (Eq. 3) instead of asymmetric (Eq. 2)
+ *   bits 8-15  restarts - 1: the whole k-means runs from that many initializations
+ *              (Philox streams t + 16 r) and the one with the lowest final objective
+ *              is kept (the earliest on ties), as scikit-learn's n_init does
+ * Any other bit set, or a field value not listed, is an invalid argument.
+ *
+ * Traces are optional (NULL to skip) and belong to the restart that is kept:
  *   c_trace [n_rows, iters+1, k]  centroids c^0 .. c^iters
  *   j_trace [n_rows, iters+1]     J at c^0 .. c^iters, each with the E-step
  *                                 assignment at those centroids
- *   picks   [n_rows, k]           k-means++ picks
+ *   picks   [n_rows, k]           initial picks (-1 where no element was drawn)
  *   c_final [n_rows, k]           fp32 centroids before the fp16 cast
  * A row with a non-finite input, a negative activation statistic, a non-finite
  * alpha or a too-large weight gets zero outputs and a NaN objective, and the call
  * returns ORACLE_ERR_NONFINITE after finishing the other rows. */
-int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n_cols,
-                         const float* act, int64_t row_offset, int32_t matrix_index,
-                         int32_t group, int32_t n_clusters, int32_t iters, uint64_t seed,
-                         uint8_t* codes, uint16_t* lut, uint16_t* scale, uint16_t* offset,
-                         double* objective, float* c_trace, double* j_trace,
-                         int32_t* picks, float* c_final) {
+int oracle_any4_quantize_v(const void* w, int32_t dtype, int64_t n_rows, int64_t n_cols,
+                           const float* act, int64_t row_offset, int32_t matrix_index,
+                           int32_t group, int32_t n_clusters, int32_t iters, uint64_t seed,
+                           int32_t variant,
+                           uint8_t* codes, uint16_t* lut, uint16_t* scale, uint16_t* offset,
+                           double* objective, float* c_trace, double* j_trace,
+                           int32_t* picks, float* c_final) {
     const int64_t K = n_cols;
     const int32_t k = n_clusters;
+    const int32_t weighting = variant & 3, init = (variant >> 2) & 3, symmetric = (variant >> 4) & 1;
+    const int32_t restarts = ((variant >> 8) & 0xFF) + 1;
     if (n_rows < 0 || K < 2 || (K & 1) || group < 1 || K % group != 0 || iters < 0 ||
         (dtype != 0 && dtype != 1) || row_offset < 0 ||
-        !(k == 2 || k == 4 || k == 8 || k == 16))
+        !(k == 2 || k == 4 || k == 8 || k == 16) || weighting == 3 || init == 3 ||
+        (variant & ~0xFF1F) != 0)
         return ORACLE_ERR_INVALID_ARG;
     const int32_t qr = k - 1;
+    const float level0 = symmetric ? (float)(1 - k / 2) : 0.0f;
     const int64_t G = K / group;
     float* wrow = (float*)malloc((size_t)K * sizeof(float));
     float* ws = (float*)malloc((size_t)K * sizeof(float));
@@ -338,8 +413,10 @@ int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n
     float* alpha = (float*)malloc((size_t)G * sizeof(float));
     float* beta = (float*)malloc((size_t)G * sizeof(float));
     uint8_t* q = (uint8_t*)malloc((size_t)K);
-    if (!wrow || !ws || !a || !alpha || !beta || !q) {
-        free(wrow); free(ws); free(a); free(alpha); free(beta); free(q);
+    float* ct = (float*)malloc((size_t)(iters + 1) * 16 * sizeof(float));
+    double* jt = (double*)malloc((size_t)(iters + 1) * sizeof(double));
+    if (!wrow || !ws || !a || !alpha || !beta || !q || !ct || !jt) {
+        free(wrow); free(ws); free(a); free(alpha); free(beta); free(q); free(ct); free(jt);
         return ORACLE_ERR_INVALID_ARG;
     }
     int status = ORACLE_OK;
@@ -350,8 +427,8 @@ int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n
             const uint16_t* wb = (const uint16_t*)w + i * K;
             for (int64_t j = 0; j < K; ++j) wrow[j] = bf16_to_f32(wb[j]);
         }
-        int bad = oracle_scale_row(wrow, K, group, qr, ws, alpha, beta);
-        bad |= oracle_weights_row(alpha, act, K, group, a);
+        int bad = oracle_scale_row_mode(wrow, K, group, qr, symmetric, ws, alpha, beta);
+        bad |= oracle_weights_row_mode(alpha, act, K, group, weighting, a);
         for (int64_t j = 0; j < K && !bad; ++j)
             if (!isfinite(a[j] * ws[j])) bad = 1;
         if (bad) {
@@ -363,31 +440,54 @@ int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n
             if (objective) objective[i] = NAN;
             continue;
         }
-        float c[16], cn[16];
-        int32_t pk[16];
-        oracle_seed_row(ws, a, K, k, seed, (uint64_t)(row_offset + i), (uint32_t)matrix_index,
-                        c, pk);
-        if (picks) memcpy(picks + i * k, pk, (size_t)k * sizeof(int32_t));
-        for (int32_t it = 0; it <= iters; ++it) {
-            oracle_estep_row(ws, K, c, k, q);
-            if (c_trace) memcpy(c_trace + (i * (iters + 1) + it) * k, c, (size_t)k * sizeof(float));
-            if (j_trace) j_trace[i * (iters + 1) + it] = oracle_objective_row(ws, a, q, K, c);
-            if (it == iters) break;
-            oracle_mstep_row(ws, a, q, K, c, k, cn);
-            memcpy(c, cn, sizeof(c));
+        float best_c[16];
+        double best_j = INFINITY;
+        for (int32_t r = 0; r < restarts; ++r) {
+            float c[16], cn[16];
+            int32_t pk[16];
+            oracle_seed_row_init(ws, a, K, k, seed, (uint64_t)(row_offset + i),
+                                 (uint32_t)matrix_index, init, r, level0, c, pk);
+            double J = 0.0;
+            for (int32_t it = 0; it <= iters; ++it) {
+                oracle_estep_row(ws, K, c, k, q);
+                memcpy(ct + (size_t)it * k, c, (size_t)k * sizeof(float));
+                jt[it] = oracle_objective_row(ws, a, q, K, c);
+                if (it == iters) { J = jt[it]; break; }
+                oracle_mstep_row(ws, a, q, K, c, k, cn);
+                memcpy(c, cn, sizeof(c));
+            }
+            if (r == 0 || J < best_j) {      /* the earliest restart wins ties */
+                best_j = J;
+                memcpy(best_c, c, sizeof(best_c));
+                if (picks) memcpy(picks + i * k, pk, (size_t)k * sizeof(int32_t));
+                if (c_trace) memcpy(c_trace + i * (iters + 1) * k, ct, (size_t)(iters + 1) * k * sizeof(float));
+                if (j_trace) memcpy(j_trace + i * (iters + 1), jt, (size_t)(iters + 1) * sizeof(double));
+            }
         }
-        /* q now holds the final E-step at c^iters */
-        if (objective) objective[i] = oracle_objective_row(ws, a, q, K, c);
-        if (c_final) memcpy(c_final + i * k, c, (size_t)k * sizeof(float));
+        /* final E-step at the kept centroids */
+        oracle_estep_row(ws, K, best_c, k, q);
+        if (objective) objective[i] = oracle_objective_row(ws, a, q, K, best_c);
+        if (c_final) memcpy(c_final + i * k, best_c, (size_t)k * sizeof(float));
         oracle_pack_row(q, K, codes + i * (K / 2));
-        for (int t = 0; t < k; ++t) lut[i * k + t] = fp16_rne(c[t]);
+        for (int t = 0; t < k; ++t) lut[i * k + t] = fp16_rne(best_c[t]);
         for (int64_t g = 0; g < G; ++g) {
             scale[i * G + g] = fp16_rne(alpha[g]);
             offset[i * G + g] = fp16_rne(beta[g]);
         }
     }
-    free(wrow); free(ws); free(a); free(alpha); free(beta); free(q);
+    free(wrow); free(ws); free(a); free(alpha); free(beta); free(q); free(ct); free(jt);
     return status;
+}
+
+int oracle_any4_quantize(const void* w, int32_t dtype, int64_t n_rows, int64_t n_cols,
+                         const float* act, int64_t row_offset, int32_t matrix_index,
+                         int32_t group, int32_t n_clusters, int32_t iters, uint64_t seed,
+                         uint8_t* codes, uint16_t* lut, uint16_t* scale, uint16_t* offset,
+                         double* objective, float* c_trace, double* j_trace,
+                         int32_t* picks, float* c_final) {
+    return oracle_any4_quantize_v(w, dtype, n_rows, n_cols, act, row_offset, matrix_index, group,
+                                  n_clusters, iters, seed, 0, codes, lut, scale, offset, objective,
+                                  c_trace, j_trace, picks, c_final);
 }
 
 /* ------------------------------------------------------------------------- */
