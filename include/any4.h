@@ -81,21 +81,44 @@ typedef struct {
   double* objective;
 } any4_matrix;
 
+/* Method variants (the paper's ablations), OR-ed into any4_params.variant; 0 selects
+ * the defaults used everywhere else in the paper. */
+enum {
+  /* sample weights (Appendix C.1, Table A3): Eq. 23's alpha * E|x| (default), E|x|
+   * alone, or none (every weight 1: plain k-means on the scaled weights) */
+  ANY4_WEIGHT_ALPHA_ACT = 0, ANY4_WEIGHT_ACT = 1, ANY4_WEIGHT_NONE = 2,
+  /* initialization (Appendix C.2, Table A4): k-means++ (default); random: k distinct
+   * elements drawn one after another with probability proportional to the sample
+   * weight (the same Philox stream); uniform: the integer levels (0..2^n-1, or
+   * 1-2^(n-1)..2^(n-1) under symmetric scaling, i.e. int4's -7..8) */
+  ANY4_INIT_KMEANSPP = 0, ANY4_INIT_RANDOM = 1 << 2, ANY4_INIT_UNIFORM = 2 << 2,
+  /* symmetric scaling (Section 2.5.1, Eq. 3): alpha = max|w| / 2^(n-1), beta = 0 */
+  ANY4_SCALE_SYMMETRIC = 1 << 4
+};
+/* restarts (n_init): the whole k-means runs from n initializations (restart r draws
+ * from Philox counters t + 16 r) and each row keeps the run with the lowest final
+ * objective (the earliest on ties).  n in 1..256; needs the larger workspace that
+ * any4_workspace_bytes reports. */
+#define ANY4_RESTARTS(n) (((n) - 1) << 8)
+
 /* group:      power of two, 2 <= group, n_cols % group == 0 (Section 2.5.1; 128 is
  *             the paper's default)
  * n_clusters: 2, 4, 8 or 16 (any1..any4; Qmax - Qmin = n_clusters - 1)
  * iters:      Lloyd rounds (E-step then M-step), >= 0, followed by one final E-step
- * seed:       Philox4x32-10 key for k-means++ */
+ * variant:    0, or ANY4_WEIGHT_* | ANY4_INIT_* | ANY4_SCALE_SYMMETRIC | ANY4_RESTARTS(n);
+ *             any other bit is an invalid argument
+ * seed:       Philox4x32-10 key for k-means++ and random initialization */
 typedef struct {
   int32_t group;
   int32_t n_clusters;
   int32_t iters;
-  int32_t reserved; /* must be 0 */
+  int32_t variant;
   uint64_t seed;
 } any4_params;
 
-/* Size of the workspace any4_quantize needs for this batch (a device status word
- * and padding).  Validates the arguments like any4_quantize. */
+/* Size of the workspace any4_quantize needs for this batch: a device status word and
+ * padding, plus, with restarts, one candidate set of outputs per matrix (codes, LUT,
+ * objectives, centroids, picks).  Validates the arguments like any4_quantize. */
 int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_params* params,
                          size_t* bytes_out);
 

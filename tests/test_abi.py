@@ -90,9 +90,15 @@ def test_workspace_query_and_validation(L):
         kw.update(pkw)
         st, _ = _ws_bytes(L, _mat(**mkw), any4.params(**kw))
         assert st == 1, (mkw, pkw)
-    pr = any4.params(128, 16, 20, 0)
-    pr.reserved = 1
-    assert _ws_bytes(L, _mat(), pr)[0] == 1
+    # variant word: unknown bits and unlisted field values are rejected
+    for v in (3, 3 << 2, 1 << 5, 1 << 16, -1):
+        assert _ws_bytes(L, _mat(), any4.params(128, 16, 20, 0, v))[0] == 1, v
+    for v in (any4.WEIGHT_ACT, any4.WEIGHT_NONE | any4.INIT_RANDOM, any4.SCALE_SYMMETRIC,
+              any4.INIT_UNIFORM | any4.SCALE_SYMMETRIC):
+        assert _ws_bytes(L, _mat(), any4.params(128, 16, 20, 0, v)) == (0, 256), v
+    # restarts need room for one candidate set of outputs per matrix
+    st, nbytes = _ws_bytes(L, _mat(n=4, k=512), any4.params(128, 16, 20, 0, any4.RESTARTS(3)))
+    assert st == 0 and nbytes >= 256 + 4 * 256 + 4 * 16 * 2 + 2 * 4 * 8 + 2 * 4 * 16 * 4
     # too long for register residency
     assert _ws_bytes(L, _mat(k=65536), p)[0] == 2
     # missing product pointer

@@ -16,6 +16,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libany4.so")
 
 ANY4_F32, ANY4_BF16 = 0, 1
+# method variants (include/any4.h): OR them into `variant`
+WEIGHT_ALPHA_ACT, WEIGHT_ACT, WEIGHT_NONE = 0, 1, 2
+INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM = 0, 1 << 2, 2 << 2
+SCALE_SYMMETRIC = 1 << 4
+
+
+def RESTARTS(n: int) -> int:
+    return (n - 1) << 8
 ANY4_OK = 0
 ANY4_ERR_NONFINITE = 5
 WORKSPACE_BYTES = 256
@@ -51,7 +59,7 @@ class Any4Params(ctypes.Structure):
         ("group", ctypes.c_int32),
         ("n_clusters", ctypes.c_int32),
         ("iters", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
     ]
 
@@ -149,8 +157,16 @@ def _dtype_code(w) -> Tuple[int, object]:
     raise TypeError(f"W must be float32 or bfloat16, got {w.dtype}")
 
 
-def params(group: int = 128, n_clusters: int = 16, iters: int = 20, seed: int = 0) -> Any4Params:
-    return Any4Params(group, n_clusters, iters, 0, seed)
+def params(group: int = 128, n_clusters: int = 16, iters: int = 20, seed: int = 0,
+           variant: int = 0) -> Any4Params:
+    return Any4Params(group, n_clusters, iters, variant, seed)
+
+
+def workspace_bytes(mats, count: int, p: Any4Params) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().any4_workspace_bytes(mats, count, ctypes.byref(p), ctypes.byref(n)),
+           "any4_workspace_bytes")
+    return n.value
 
 
 @dataclass
@@ -193,23 +209,24 @@ def _matrix(w, act, out: Optional[Quantized], row_offset=0, matrix_index=0) -> A
     return m
 
 
-def workspace(device=None):
+def workspace(device=None, nbytes: int = WORKSPACE_BYTES):
     torch = _torch()
-    return torch.empty((WORKSPACE_BYTES,), dtype=torch.uint8, device=device or "cuda")
+    return torch.empty((max(nbytes, WORKSPACE_BYTES),), dtype=torch.uint8, device=device or "cuda")
 
 
 def quantize_batch(items: Sequence[Tuple[object, object]], group: int = 128, n_clusters: int = 16,
                    iters: int = 20, seed: int = 0, with_objective: bool = True,
                    outputs: Optional[List[Quantized]] = None, ws=None,
                    row_offsets: Optional[Sequence[int]] = None,
-                   matrix_indices: Optional[Sequence[int]] = None) -> List[Quantized]:
+                   matrix_indices: Optional[Sequence[int]] = None,
+                   variant: int = 0) -> List[Quantized]:
     """Quantize several (W [N,K], act_absmean [K]) pairs in one call."""
     if not items:
         return []
     w0 = items[0][0]
     _require_gpu(w0)
     device = w0.device
-    p = params(group, n_clusters, iters, seed)
+    p = params(group, n_clusters, iters, seed, variant)
     if outputs is None:
         outputs = [_alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, device, with_objective)
                    for w, _ in items]
@@ -218,8 +235,9 @@ def quantize_batch(items: Sequence[Tuple[object, object]], group: int = 128, n_c
         mats[i] = _matrix(w, act, outputs[i],
                           row_offset=(row_offsets[i] if row_offsets else 0),
                           matrix_index=(matrix_indices[i] if matrix_indices else i))
-    if ws is None:
-        ws = workspace(device)
+    need = workspace_bytes(mats, len(items), p)
+    if ws is None or ws.numel() < need:
+        ws = workspace(device, need)
     _check(lib().any4_quantize(mats, len(items), ctypes.byref(p), _ptr(ws), ws.numel(),
                                _stream(device)), "any4_quantize")
     return outputs
@@ -227,15 +245,17 @@ def quantize_batch(items: Sequence[Tuple[object, object]], group: int = 128, n_c
 
 def quantize(w, act, group: int = 128, n_clusters: int = 16, iters: int = 20, seed: int = 0,
              row_offset: int = 0, matrix_index: int = 0, with_objective: bool = True,
-             out: Optional[Quantized] = None, ws=None) -> Quantized:
-    """Quantize one matrix W [N,K] (bf16/fp32) with E|x| act [K] (fp32)."""
+             out: Optional[Quantized] = None, ws=None, variant: int = 0) -> Quantized:
+    """Quantize one matrix W [N,K] (bf16/fp32) with E|x| act [K] (fp32).  `variant`
+    selects the paper's ablated variants (WEIGHT_*, INIT_*, SCALE_SYMMETRIC, RESTARTS(n))."""
     _require_gpu(w)
-    p = params(group, n_clusters, iters, seed)
+    p = params(group, n_clusters, iters, seed, variant)
     if out is None:
         out = _alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, w.device, with_objective)
     m = _matrix(w, act, out, row_offset, matrix_index)
-    if ws is None:
-        ws = workspace(w.device)
+    need = WORKSPACE_BYTES if variant >> 8 == 0 else workspace_bytes(ctypes.byref(m), 1, p)
+    if ws is None or ws.numel() < need:
+        ws = workspace(w.device, need)
     _check(lib().any4_quantize(ctypes.byref(m), 1, ctypes.byref(p), _ptr(ws), ws.numel(),
                                _stream(w.device)), "any4_quantize")
     return out
@@ -298,7 +318,7 @@ def dequantize(q: Quantized, group: int = 128, n_clusters: int = 16, out_dtype=N
 # ---------------------------------------------------------------------------------
 # stage entry points (parity tests)
 
-def stage_scale(w, act, group=128, n_clusters=16, row_offset=0, matrix_index=0):
+def stage_scale(w, act, group=128, n_clusters=16, row_offset=0, matrix_index=0, variant=0):
     torch = _torch()
     _require_gpu(w)
     N, K = w.shape
@@ -308,26 +328,26 @@ def stage_scale(w, act, group=128, n_clusters=16, row_offset=0, matrix_index=0):
     be = torch.empty((N, K // group), dtype=torch.float32, device=dev)
     a = torch.empty((N, K), dtype=torch.float32, device=dev)
     m = _matrix(w, act, None, row_offset, matrix_index)
-    p = params(group, n_clusters, 0, 0)
+    p = params(group, n_clusters, 0, 0, variant)
     _check(lib().any4_stage_scale(ctypes.byref(m), ctypes.byref(p), _ptr(ws_), _ptr(al), _ptr(be),
                                   _ptr(a), _stream(dev)), "any4_stage_scale")
     return ws_, al, be, a
 
 
-def stage_seed(w, act, group=128, n_clusters=16, seed=0, row_offset=0, matrix_index=0):
+def stage_seed(w, act, group=128, n_clusters=16, seed=0, row_offset=0, matrix_index=0, variant=0):
     torch = _torch()
     _require_gpu(w)
     N = w.shape[0]
     c0 = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
     picks = torch.empty((N, n_clusters), dtype=torch.int32, device=w.device)
     m = _matrix(w, act, None, row_offset, matrix_index)
-    p = params(group, n_clusters, 0, seed)
+    p = params(group, n_clusters, 0, seed, variant)
     _check(lib().any4_stage_seed(ctypes.byref(m), ctypes.byref(p), _ptr(c0), _ptr(picks),
                                  _stream(w.device)), "any4_stage_seed")
     return c0, picks
 
 
-def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16):
+def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16, variant=0):
     torch = _torch()
     _require_gpu(w)
     N, K = w.shape
@@ -335,7 +355,7 @@ def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16):
     c_out = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
     obj = torch.empty((N,), dtype=torch.float64, device=w.device)
     m = _matrix(w, act, None)
-    p = params(group, n_clusters, 1, 0)
+    p = params(group, n_clusters, 1, 0, variant)
     c_in = c_in.contiguous().to(torch.float32)
     _check(lib().any4_stage_lloyd_step(ctypes.byref(m), ctypes.byref(p), _ptr(c_in), _ptr(assign),
                                        _ptr(c_out), _ptr(obj), _stream(w.device)),
@@ -357,7 +377,8 @@ def stage_pack(n_rows, n_cols, assign, c, alpha, beta, group=128, n_clusters=16)
     return out
 
 
-def stage_full(w, act, group=128, n_clusters=16, iters=20, seed=0, row_offset=0, matrix_index=0):
+def stage_full(w, act, group=128, n_clusters=16, iters=20, seed=0, row_offset=0, matrix_index=0,
+               variant=0):
     """Full path for one matrix plus the fp32 final centroids and the k-means++ picks."""
     torch = _torch()
     _require_gpu(w)
@@ -366,8 +387,8 @@ def stage_full(w, act, group=128, n_clusters=16, iters=20, seed=0, row_offset=0,
     c_final = torch.empty((N, n_clusters), dtype=torch.float32, device=w.device)
     picks = torch.empty((N, n_clusters), dtype=torch.int32, device=w.device)
     m = _matrix(w, act, out, row_offset, matrix_index)
-    p = params(group, n_clusters, iters, seed)
-    ws = workspace(w.device)
+    p = params(group, n_clusters, iters, seed, variant)
+    ws = workspace(w.device, workspace_bytes(ctypes.byref(m), 1, p))
     _check(lib().any4_stage_full(ctypes.byref(m), ctypes.byref(p), _ptr(c_final), _ptr(picks),
                                  _ptr(ws), ws.numel(), _stream(w.device)), "any4_stage_full")
     return out, c_final, picks, ws

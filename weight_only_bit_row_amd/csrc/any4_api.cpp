@@ -26,8 +26,50 @@ int check_params(const any4_params* p) {
   if (p->group < 2 || !is_pow2(p->group)) return ANY4_ERR_INVALID_ARG;
   if (!(p->n_clusters == 2 || p->n_clusters == 4 || p->n_clusters == 8 || p->n_clusters == 16))
     return ANY4_ERR_INVALID_ARG;
-  if (p->iters < 0 || p->reserved != 0) return ANY4_ERR_INVALID_ARG;
+  if (p->iters < 0) return ANY4_ERR_INVALID_ARG;
+  if ((p->variant & ~any4::kVarKnownBits) != 0) return ANY4_ERR_INVALID_ARG;
+  if ((p->variant & any4::kVarWeightMask) == 3) return ANY4_ERR_INVALID_ARG;
+  if (((p->variant >> any4::kVarInitShift) & 3) == 3) return ANY4_ERR_INVALID_ARG;
   return ANY4_OK;
+}
+
+int restarts_of(const any4_params* p) { return ((p->variant >> any4::kVarRestartShift) & 0xFF) + 1; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace carved per matrix for restarts > 1: a candidate restart's codes, LUT,
+// objective, fp32 centroids and picks, and the best objective so far.
+struct RestartBufs {
+  uint8_t* codes;
+  uint16_t* lut;
+  double* obj;
+  float* c;
+  int32_t* picks;
+  double* best_obj;
+};
+
+size_t restart_bytes(const any4_matrix* m, int k) {
+  const size_t n = static_cast<size_t>(m->n_rows);
+  return align256(n * static_cast<size_t>(m->n_cols / 2)) + align256(n * k * 2) +
+         2 * align256(n * 8) + 2 * align256(n * k * 4);
+}
+
+RestartBufs carve_restart(unsigned char*& base, const any4_matrix* m, int k) {
+  const size_t n = static_cast<size_t>(m->n_rows);
+  RestartBufs b;
+  b.codes = base;
+  base += align256(n * static_cast<size_t>(m->n_cols / 2));
+  b.lut = reinterpret_cast<uint16_t*>(base);
+  base += align256(n * k * 2);
+  b.obj = reinterpret_cast<double*>(base);
+  base += align256(n * 8);
+  b.c = reinterpret_cast<float*>(base);
+  base += align256(n * k * 4);
+  b.picks = reinterpret_cast<int32_t*>(base);
+  base += align256(n * k * 4);
+  b.best_obj = reinterpret_cast<double*>(base);
+  base += align256(n * 8);
+  return b;
 }
 
 int check_matrix(const any4_matrix* m, const any4_params* p, bool need_products) {
@@ -70,6 +112,8 @@ LaunchArgs make_args(const any4_params* p, int nw, uint32_t* status) {
   a.n_clusters = p->n_clusters;
   a.iters = p->iters;
   a.nw = nw;
+  a.variant = p->variant & ((1 << any4::kVarRestartShift) - 1);
+  a.restart = 0;
   a.seed = p->seed;
   a.status = status;
   return a;
@@ -129,7 +173,10 @@ int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_para
   if (!bytes_out) return ANY4_ERR_INVALID_ARG;
   const int st = validate_batch(mats, count, params);
   if (st != ANY4_OK) return st;
-  *bytes_out = kWorkspaceBytes;
+  size_t bytes = kWorkspaceBytes;
+  if (restarts_of(params) > 1)
+    for (int32_t i = 0; i < count; ++i) bytes += restart_bytes(&mats[i], params->n_clusters);
+  *bytes_out = bytes;
   return ANY4_OK;
 }
 
@@ -137,9 +184,18 @@ int any4_quantize(const any4_matrix* mats, int32_t count, const any4_params* par
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = validate_batch(mats, count, params);
   if (st != ANY4_OK) return st;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return ANY4_ERR_WORKSPACE;
+  size_t need = 0;
+  any4_workspace_bytes(mats, count, params, &need);
+  if (!workspace || workspace_bytes < need) return ANY4_ERR_WORKSPACE;
   uint32_t* status = static_cast<uint32_t*>(workspace);
   if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
+  const int R = restarts_of(params);
+  const int k = params->n_clusters;
+  std::vector<RestartBufs> rb(static_cast<size_t>(count));
+  if (R > 1) {
+    unsigned char* base = static_cast<unsigned char*>(workspace) + kWorkspaceBytes;
+    for (int32_t i = 0; i < count; ++i) rb[i] = carve_restart(base, &mats[i], k);
+  }
 
   // Matrices sharing a row geometry go into one launch (up to kMaxMats each);
   // longer rows first so that the longest blocks start earliest.
@@ -149,25 +205,60 @@ int any4_quantize(const any4_matrix* mats, int32_t count, const any4_params* par
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
     return mats[x].n_cols > mats[y].n_cols;
   });
-  size_t i = 0;
-  while (i < order.size()) {
-    const RowConfig cfg = any4::choose_config(mats[order[i]].n_cols);
-    LaunchArgs a = make_args(params, cfg.nw, status);
-    int64_t rows = 0;
-    a.n_mats = 0;
-    while (i < order.size() && a.n_mats < any4::kMaxMats) {
-      const RowConfig c2 = any4::choose_config(mats[order[i]].n_cols);
-      if (c2.e != cfg.e || c2.nw != cfg.nw) break;
-      if (rows + mats[order[i]].n_rows > INT32_MAX) break;
-      a.row_start[a.n_mats] = rows;
-      a.m[a.n_mats] = make_desc(&mats[order[i]]);
-      rows += mats[order[i]].n_rows;
-      ++a.n_mats;
-      ++i;
+  // Restart r (Philox counters t + 16 r): the first writes the outputs, each later one
+  // writes candidates that replace a row's outputs where its objective is lower.
+  for (int r = 0; r < R; ++r) {
+    size_t i = 0;
+    while (i < order.size()) {
+      const RowConfig cfg = any4::choose_config(mats[order[i]].n_cols);
+      LaunchArgs a = make_args(params, cfg.nw, status);
+      a.restart = r;
+      int64_t rows = 0;
+      a.n_mats = 0;
+      while (i < order.size() && a.n_mats < any4::kMaxMats) {
+        const RowConfig c2 = any4::choose_config(mats[order[i]].n_cols);
+        if (c2.e != cfg.e || c2.nw != cfg.nw) break;
+        if (rows + mats[order[i]].n_rows > INT32_MAX) break;
+        const any4_matrix* m = &mats[order[i]];
+        MatDesc d = make_desc(m);
+        if (R > 1) {
+          const RestartBufs& b = rb[order[i]];
+          double* best = m->objective ? m->objective : b.best_obj;
+          if (r == 0) {
+            d.objective = best;
+          } else {
+            d.codes = b.codes;
+            d.lut = b.lut;
+            d.objective = b.obj;
+          }
+        }
+        a.row_start[a.n_mats] = rows;
+        a.m[a.n_mats] = d;
+        rows += m->n_rows;
+        ++a.n_mats;
+        ++i;
+      }
+      for (int j = a.n_mats; j <= any4::kMaxMats; ++j) a.row_start[j] = rows;
+      if (any4::launch_rows(a, cfg, any4::MODE_FULL, rows, stream) != hipSuccess)
+        return ANY4_ERR_HIP;
     }
-    for (int j = a.n_mats; j <= any4::kMaxMats; ++j) a.row_start[j] = rows;
-    if (any4::launch_rows(a, cfg, any4::MODE_FULL, rows, stream) != hipSuccess)
-      return ANY4_ERR_HIP;
+    if (r == 0) continue;
+    for (int32_t idx : order) {
+      const any4_matrix* m = &mats[idx];
+      const RestartBufs& b = rb[idx];
+      any4::MergeDesc md;
+      std::memset(&md, 0, sizeof(md));
+      md.n_rows = m->n_rows;
+      md.n_cols = m->n_cols;
+      md.n_clusters = k;
+      md.cand_codes = b.codes;
+      md.cand_lut = b.lut;
+      md.cand_obj = b.obj;
+      md.codes = m->codes;
+      md.lut = m->lut;
+      md.best_obj = m->objective ? m->objective : b.best_obj;
+      if (any4::launch_restart_merge(md, stream) != hipSuccess) return ANY4_ERR_HIP;
+    }
   }
   return ANY4_OK;
 }
@@ -240,13 +331,56 @@ int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_fi
                     int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = validate_batch(m, 1, params);
   if (st != ANY4_OK) return st;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return ANY4_ERR_WORKSPACE;
+  size_t need = 0;
+  any4_workspace_bytes(m, 1, params, &need);
+  if (!workspace || workspace_bytes < need) return ANY4_ERR_WORKSPACE;
   uint32_t* status = static_cast<uint32_t*>(workspace);
   if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
-  MatDesc d = make_desc(m);
-  d.c_out = c_final;
-  d.picks_out = picks;
-  return launch_one(make_args(params, 1, status), d, any4::MODE_FULL, stream);
+  const int R = restarts_of(params);
+  RestartBufs b{};
+  if (R > 1) {
+    unsigned char* base = static_cast<unsigned char*>(workspace) + kWorkspaceBytes;
+    b = carve_restart(base, m, params->n_clusters);
+  }
+  double* best = m->objective ? m->objective : b.best_obj;
+  for (int r = 0; r < R; ++r) {
+    MatDesc d = make_desc(m);
+    d.c_out = c_final;
+    d.picks_out = picks;
+    if (R > 1) {
+      if (r == 0) {
+        d.objective = best;
+      } else {
+        d.codes = b.codes;
+        d.lut = b.lut;
+        d.objective = b.obj;
+        d.c_out = c_final ? b.c : nullptr;
+        d.picks_out = picks ? b.picks : nullptr;
+      }
+    }
+    LaunchArgs a = make_args(params, 1, status);
+    a.restart = r;
+    st = launch_one(a, d, any4::MODE_FULL, stream);
+    if (st != ANY4_OK) return st;
+    if (r == 0 || m->n_rows == 0) continue;
+    any4::MergeDesc md;
+    std::memset(&md, 0, sizeof(md));
+    md.n_rows = m->n_rows;
+    md.n_cols = m->n_cols;
+    md.n_clusters = params->n_clusters;
+    md.cand_codes = b.codes;
+    md.cand_lut = b.lut;
+    md.cand_obj = b.obj;
+    md.cand_c = c_final ? b.c : nullptr;
+    md.cand_picks = picks ? b.picks : nullptr;
+    md.codes = m->codes;
+    md.lut = m->lut;
+    md.best_obj = best;
+    md.c = c_final;
+    md.picks = picks;
+    if (any4::launch_restart_merge(md, stream) != hipSuccess) return ANY4_ERR_HIP;
+  }
+  return ANY4_OK;
 }
 
 int any4_act_absmean_workspace_bytes(int64_t n_tokens, int64_t n_cols, size_t* bytes_out) {

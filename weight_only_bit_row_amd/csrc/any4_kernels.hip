@@ -234,48 +234,72 @@ __device__ __forceinline__ bool right_wins(float x, float cl, int il, float cr, 
   return dr < dl || (dr == dl && ir < il);
 }
 
-// Smallest fp32 x in [cl, cr] (0 <= cl < cr) at which R wins.  The rule is monotone
-// in x on that interval (left distance non-decreasing, right non-increasing under
-// monotone rounding), so the winners form a suffix of the ordered bit patterns.  The
-// answer lies within a few ulps of the rounded midpoint: the five patterns mb-2..mb+2
-// are tested independently, and when mb-2 loses and mb+2 wins the answer is mb-2 plus
-// the number of losers.  Otherwise a bisection over the bit patterns decides (exact).
+// Bisection over floats by an integer key that orders like the values: for
+// non-negative floats the bit pattern itself; with SIGNED (symmetric scaling, where the
+// scaled weights can be negative) the sign-flipped pattern, so that -0 sits just below
+// +0 and negative values order by their magnitude reversed.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if (!SIGNED) return b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+template <bool SIGNED>
+__device__ __forceinline__ float key_float(uint32_t k) {
+  if (!SIGNED) return __uint_as_float(k);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Smallest fp32 x in [cl, cr] (cl < cr; both >= 0 unless SIGNED) at which R wins.  The
+// rule is monotone in x on that interval (left distance non-decreasing, right
+// non-increasing under monotone rounding), so the winners form a suffix of the ordered
+// keys.  The answer lies within a few ulps of the rounded midpoint: the five keys
+// mb-2..mb+2 are tested independently, and when mb-2 loses and mb+2 wins the answer is
+// mb-2 plus the number of losers.  Otherwise a bisection over the keys decides (exact).
+template <bool SIGNED>
 __device__ float switch_point(float cl, int il, float cr, int ir) {
-  uint32_t lo = __float_as_uint(cl), hi = __float_as_uint(cr);
+  uint32_t lo = order_key<SIGNED>(cl), hi = order_key<SIGNED>(cr);
   const float mid = cl + 0.5f * (cr - cl);
-  const uint32_t mb = __float_as_uint(mid);
+  const uint32_t mb = order_key<SIGNED>(mid);
   if (mb >= lo + 2 && mb + 2 <= hi) {
     uint32_t losers = 0;
     bool w0 = false, w4 = false;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-      const bool w = right_wins(__uint_as_float(mb - 2 + j), cl, il, cr, ir);
+      const bool w = right_wins(key_float<SIGNED>(mb - 2 + j), cl, il, cr, ir);
       losers += w ? 0u : 1u;
       if (j == 0) w0 = w;
       if (j == 4) w4 = w;
     }
-    if (!w0 && w4) return __uint_as_float(mb - 2 + losers);
+    if (!w0 && w4) return key_float<SIGNED>(mb - 2 + losers);
   }
-  if (mb >= lo + 2 && !right_wins(__uint_as_float(mb - 2), cl, il, cr, ir)) lo = mb - 1;
-  if (mb + 2 <= hi && right_wins(__uint_as_float(mb + 2), cl, il, cr, ir)) hi = mb + 2;
+  if (mb >= lo + 2 && !right_wins(key_float<SIGNED>(mb - 2), cl, il, cr, ir)) lo = mb - 1;
+  if (mb + 2 <= hi && right_wins(key_float<SIGNED>(mb + 2), cl, il, cr, ir)) hi = mb + 2;
   // invariant: every x below lo loses (or lo == cl), and hi wins (or hi == cr)
   for (int guard = 0; guard < 40 && lo < hi; ++guard) {
     const uint32_t m = lo + ((hi - lo) >> 1);
-    if (right_wins(__uint_as_float(m), cl, il, cr, ir))
+    if (right_wins(key_float<SIGNED>(m), cl, il, cr, ir))
       hi = m;
     else
       lo = m + 1;
   }
-  return __uint_as_float(hi);
+  return key_float<SIGNED>(hi);
 }
 
-// Fixed grid over the scaled range: cell h holds x in [h/2, (h+1)/2).  x * 2 is exact,
-// so the cell is monotone in x; values past the last cell clamp into it.  With at most
+__device__ __forceinline__ float switch_point_any(float cl, int il, float cr, int ir, bool sgn) {
+  return sgn ? switch_point<true>(cl, il, cr, ir) : switch_point<false>(cl, il, cr, ir);
+}
+
+// Fixed grid over the scaled range: cell h holds x with x + off in [h/2, (h+1)/2), where
+// off = 0 for asymmetric scaling (w_S in [0, 2^n - 1]) and 2^(n-1) for symmetric scaling
+// (w_S in [-2^(n-1), 2^(n-1)]).  fl(x + off) * 2 is monotone in x, so the cell is too;
+// values past either end clamp into the end cells.  With at most
 // 32 cells of 8 bytes the whole table spans each LDS bank pair once, so the gathers of
 // the E-step are free of bank conflicts (equal cells are broadcast).
-__device__ __forceinline__ uint32_t cell_of(float x, int G) {
-  const uint32_t h = static_cast<uint32_t>(x * static_cast<float>(kCellsPerUnit));
-  return h < static_cast<uint32_t>(G) ? h : static_cast<uint32_t>(G - 1);
+__device__ __forceinline__ uint32_t cell_of(float x, int G, float off) {
+  const float y = (off != 0.0f) ? x + off : x;
+  const int h = static_cast<int>(y * static_cast<float>(kCellsPerUnit));
+  return static_cast<uint32_t>(h < 0 ? 0 : (h < G ? h : G - 1));
 }
 
 // Wave 0 only: from S.c (k values), build the sorted distinct values, their lowest
@@ -283,7 +307,7 @@ __device__ __forceinline__ uint32_t cell_of(float x, int G) {
 // centroids are broadcast to uniform registers; each lane ranks its own centroid.
 // Lane t < U - 1 returns switch point t and its cell in (t_out, tc_out), lane p < U the
 // sorted value p and its draw index in (sv_out, si_out); returns U.
-__device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, uint32_t& tc_out,
+__device__ int build_structure(Smem& S, int k, int G, float off, int lane, float& t_out, uint32_t& tc_out,
                                float& sv_out, int& si_out) {
   const float inf = __builtin_huge_valf();
   float ct = (lane < k) ? S.c[lane] : inf;
@@ -309,8 +333,8 @@ __device__ int build_structure(Smem& S, int k, int G, int lane, float& t_out, ui
   float t = inf;
   uint32_t tc = kMaxCells;
   if (lane + 1 < U) {
-    t = switch_point(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1]);
-    tc = cell_of(t, G);
+    t = switch_point_any(S.sv[lane], S.sidx[lane], S.sv[lane + 1], S.sidx[lane + 1], off != 0.0f);
+    tc = cell_of(t, G, off);
   }
   sv_out = (lane < U) ? S.sv[lane] : inf;
   si_out = (lane < U) ? S.sidx[lane] : 0;
@@ -431,14 +455,27 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
   }
 }
 
-// Eq. 1-2 on one group held in registers [m0, m0+G), then the Eq. 23 sample weights.
+// Scaling of a call: Qmax - Qmin = qr = 2^n - 1 (Eq. 2), Qmax = qmax = 2^(n-1) for the
+// symmetric variant (Eq. 3), and the variant word (sample-weight term, symmetric bit).
+struct ScaleParams {
+  float qr;
+  float qmax;
+  int32_t variant;
+};
+
+// Eq. 1-2 (or Eq. 3) on one group held in registers [m0, m0+G), then the sample weights
+// of Eq. 23 (alpha * E|x|, or the ablated terms of Appendix C.1: E|x| alone, or 1).
 // Writes alpha/beta of the group (fp32 for the scale stage, fp16 otherwise).
 template <int MODE>
-__device__ __forceinline__ void finish_group(float mn, float mx, float qr, float* x, float* act,
-                                             int n, bool& bad, const MatDesc& M, int64_t row,
-                                             int64_t gidx, int64_t n_groups, bool writer) {
-  const float alpha = (mx - mn) / qr;
-  const float beta = mn;
+__device__ __forceinline__ void finish_group(float mn, float mx, const ScaleParams& sp, float* x,
+                                             float* act, int n, bool& bad, const MatDesc& M,
+                                             int64_t row, int64_t gidx, int64_t n_groups,
+                                             bool writer) {
+  const bool sym = (sp.variant & kVarSymmetric) != 0;
+  // symmetric: max|w| of the group is the larger magnitude of its extremes
+  const float alpha = sym ? fmaxf(fabsf(mn), fabsf(mx)) / sp.qmax : (mx - mn) / sp.qr;
+  const float beta = sym ? 0.0f : mn;
+  const int wmode = sp.variant & kVarWeightMask;
   if (!is_finite(alpha)) bad = true;
   for (int m = 0; m < n; ++m) {
     asm volatile("" : "+v"(x[m]), "+v"(act[m]));  // one division in flight at a time
@@ -447,7 +484,7 @@ __device__ __forceinline__ void finish_group(float mn, float mx, float qr, float
       const float diff = x[m] - beta;
       ws = diff / alpha;
     }
-    const float a = alpha * act[m];
+    const float a = (wmode == 0) ? alpha * act[m] : (wmode == 1 ? act[m] : 1.0f);
     if (!is_finite(a) || a > kAMax || !is_finite(a * ws)) bad = true;
     x[m] = ws;
     act[m] = a;
@@ -465,7 +502,7 @@ __device__ __forceinline__ void finish_group(float mn, float mx, float qr, float
 
 // Groups no wider than a lane's E columns: G is a compile-time group size.
 template <int E, int G, int MODE>
-__device__ __forceinline__ void scale_narrow(float (&x)[E], float (&act)[E], float qr, int K,
+__device__ __forceinline__ void scale_narrow(float (&x)[E], float (&act)[E], const ScaleParams& sp, int K,
                                              int col0, bool& bad, const MatDesc& M, int64_t row,
                                              int g) {
   const int64_t n_groups = K / g;
@@ -479,7 +516,7 @@ __device__ __forceinline__ void scale_narrow(float (&x)[E], float (&act)[E], flo
       mx = fmaxf(mx, x[lg * G + m]);
     }
     if (valid) {
-      finish_group<MODE>(mn, mx, qr, &x[lg * G], &act[lg * G], G, bad, M, row,
+      finish_group<MODE>(mn, mx, sp, &x[lg * G], &act[lg * G], G, bad, M, row,
                          (col0 + lg * G) / g, n_groups, true);
     } else {
 #pragma unroll
@@ -493,7 +530,7 @@ __device__ __forceinline__ void scale_narrow(float (&x)[E], float (&act)[E], flo
 
 // Groups spanning L = g / E lanes (L a power of two, lanes aligned to the group).
 template <int E, int MODE>
-__device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], float qr, int K,
+__device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], const ScaleParams& sp, int K,
                                            int col0, bool& bad, const MatDesc& M, int64_t row,
                                            int g, Smem& S, int lane, int wave, int nw) {
   const bool valid = col0 < K;
@@ -535,7 +572,7 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], float
     __syncthreads();
   }
   if (valid) {
-    finish_group<MODE>(mn, mx, qr, x, act, E, bad, M, row, col0 / g, K / g, (col0 % g) == 0);
+    finish_group<MODE>(mn, mx, sp, x, act, E, bad, M, row, col0 / g, K / g, (col0 % g) == 0);
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
@@ -670,7 +707,7 @@ __device__ __forceinline__ void zero_bins(double* bins, int lane) {
 // unchanged: only the values and the switch points are recomputed, the right neighbour
 // coming from the next lane by DPP.  Otherwise the structure is rebuilt from the
 // draw-order centroids.  Returns U; (t, tc) as in build_structure.
-__device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int G, int lane, int U,
+__device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int G, float off, int lane, int U,
                                                     float& sv, int& si, float& t,
                                                     uint32_t& tc) {
   float cn = sv;
@@ -690,8 +727,8 @@ __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int 
     t = __builtin_huge_valf();
     tc = kMaxCells;
     if (lane + 1 < U) {
-      t = switch_point(cn, si, cnext, inext);
-      tc = cell_of(t, G);
+      t = switch_point_any(cn, si, cnext, inext, off != 0.0f);
+      tc = cell_of(t, G, off);
     }
     sv = cn;
     if (lane < U) S.sv[lane] = cn;
@@ -703,7 +740,7 @@ __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int 
     return U;
   }
   wave_lds_fence();
-  return build_structure(S, k, G, lane, t, tc, sv, si);
+  return build_structure(S, k, G, off, lane, t, tc, sv, si);
 }
 
 __device__ __forceinline__ float block_max(float v, Smem& S, int lane, int wave, int nw,
@@ -738,8 +775,10 @@ struct WavesPerEU {
 
 // WIDE: the group is at least as wide as a lane's E columns (one group per lane); the
 // kernel is instantiated separately for narrower groups so that neither carries the
-// other's scaling code.
-template <int E, int NWMAX, int MODE, bool WIDE>
+// other's scaling code.  VAR: the instance that honours the method-variant word and the
+// restart index; without it every variant branch folds away and the default path keeps
+// its own register allocation.
+template <int E, int NWMAX, int MODE, bool WIDE, bool VAR>
 __global__ __launch_bounds__(kWave* NWMAX)
 __attribute__((amdgpu_waves_per_eu(WavesPerEU<E>::value == 0 ? 1 : WavesPerEU<E>::value)))
 void any4_rows_kernel(const LaunchArgs args) {
@@ -761,6 +800,12 @@ void any4_rows_kernel(const LaunchArgs args) {
   const int g = args.group;
   const int k = args.n_clusters;
   const float qr = static_cast<float>(k - 1);
+  const int32_t variant = VAR ? args.variant : 0;
+  const int restart = VAR ? args.restart : 0;
+  const ScaleParams sp{qr, static_cast<float>(k / 2), variant};
+  const int init = (variant >> kVarInitShift) & 3;
+  // symmetric scaling puts w_S in [-k/2, k/2]: the cell grid starts at -k/2
+  const float cell_off = (variant & kVarSymmetric) ? static_cast<float>(k / 2) : 0.0f;
   const int col0 = tid * E;
 
   const int n_valid = (K - col0 < E) ? (K - col0 > 0 ? K - col0 : 0) : E;  // valid columns here
@@ -778,14 +823,14 @@ void any4_rows_kernel(const LaunchArgs args) {
 
   // ---- Eq. 1-2 scaling and Eq. 23 sample weights
   if constexpr (WIDE) {
-    scale_wide<E, MODE>(xv, av, qr, K, col0, bad, M, row, g, S, lane, wave, nw);
+    scale_wide<E, MODE>(xv, av, sp, K, col0, bad, M, row, g, S, lane, wave, nw);
   } else {
     switch (g) {
-      case 2: scale_narrow<E, 2, MODE>(xv, av, qr, K, col0, bad, M, row, g); break;
-      case 4: scale_narrow<E, 4, MODE>(xv, av, qr, K, col0, bad, M, row, g); break;
-      case 8: if constexpr (E > 8) scale_narrow<E, 8, MODE>(xv, av, qr, K, col0, bad, M, row, g); break;
-      case 16: if constexpr (E > 16) scale_narrow<E, 16, MODE>(xv, av, qr, K, col0, bad, M, row, g); break;
-      case 32: if constexpr (E > 32) scale_narrow<E, 32, MODE>(xv, av, qr, K, col0, bad, M, row, g); break;
+      case 2: scale_narrow<E, 2, MODE>(xv, av, sp, K, col0, bad, M, row, g); break;
+      case 4: scale_narrow<E, 4, MODE>(xv, av, sp, K, col0, bad, M, row, g); break;
+      case 8: if constexpr (E > 8) scale_narrow<E, 8, MODE>(xv, av, sp, K, col0, bad, M, row, g); break;
+      case 16: if constexpr (E > 16) scale_narrow<E, 16, MODE>(xv, av, sp, K, col0, bad, M, row, g); break;
+      case 32: if constexpr (E > 32) scale_narrow<E, 32, MODE>(xv, av, sp, K, col0, bad, M, row, g); break;
       default: break;
     }
   }
@@ -833,10 +878,27 @@ void any4_rows_kernel(const LaunchArgs args) {
   if (MODE == MODE_STEP) {
     if (tid < k) S.c[tid] = M.c_in[row * k + tid];
     __syncthreads();
+  } else if (init == INIT_UNIFORM) {
+    // Appendix C.2's uniform initialization: the integer levels, 0..2^n - 1 for
+    // asymmetric scaling and 1 - 2^(n-1)..2^(n-1) (int4's -7..8) for symmetric; no draws
+    if (tid < k) {
+      S.c[tid] = (cell_off != 0.0f ? 1.0f - cell_off : 0.0f) + static_cast<float>(tid);
+      S.picks[tid] = -1;
+    }
+    __syncthreads();
+    if (MODE == MODE_SEED) {
+      if (tid < k) {
+        M.c_out[row * k + tid] = S.c[tid];
+        M.picks_out[row * k + tid] = -1;
+      }
+      return;
+    }
+    if (M.picks_out && tid < k) M.picks_out[row * k + tid] = -1;
   } else {
     if (tid < k) {
       const uint64_t rid = static_cast<uint64_t>(M.row_offset + row);
-      uint32_t c[4] = {static_cast<uint32_t>(rid), static_cast<uint32_t>(tid),
+      // restart r draws from the counters t + 16 r
+      uint32_t c[4] = {static_cast<uint32_t>(rid), static_cast<uint32_t>(tid + 16 * restart),
                        static_cast<uint32_t>(M.matrix_index), static_cast<uint32_t>(rid >> 32)};
       philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
       S.u[tid] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
@@ -920,7 +982,16 @@ void any4_rows_kernel(const LaunchArgs args) {
       // order of their bit patterns as signed integers: min and max run as integer ops,
       // which need no NaN quieting of their operands.
       int imax = 0;
-      if (t == 0) {
+      if (init == INIT_RANDOM) {
+        // random initialization (Appendix C.2): the drawn element leaves the pool, the
+        // others keep their weight a_j
+        const int pm = pick - tid * E;  // no draw (pick < 0) never matches
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          if (m == pm) pv[m] = 0.0f;
+          imax = max(imax, __float_as_int(pv[m]));
+        }
+      } else if (t == 0) {
 #pragma unroll
         for (int m = 0; m < E; ++m) {
           float d = xv[m] - ct;
@@ -959,7 +1030,7 @@ void any4_rows_kernel(const LaunchArgs args) {
   for (int i = 0; i < CellWords<E>::value; ++i) cw[i] = 0;
 #pragma unroll
   for (int m = 0; m < E; ++m)
-    cw[m / kCellsPerWord] |= (cell_of(xv[m], G) * kCellBytes) << (8 * (m % kCellsPerWord));
+    cw[m / kCellsPerWord] |= (cell_of(xv[m], G, cell_off) * kCellBytes) << (8 * (m % kCellsPerWord));
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  wave * (2 * kMaxClusters * kBinCols);
   uint32_t packed[E / 8];
@@ -976,7 +1047,7 @@ void any4_rows_kernel(const LaunchArgs args) {
   if (wave == 0) {
     float t;
     uint32_t tc;
-    U = build_structure(S, k, G, lane, t, tc, sv, si);
+    U = build_structure(S, k, G, cell_off, lane, t, tc, sv, si);
     build_table(S, table, lane, t, tc, U);
   }
   __syncthreads();
@@ -1007,7 +1078,7 @@ void any4_rows_kernel(const LaunchArgs args) {
     if (wave == 0) {
       float t;
       uint32_t tc;
-      U = update_and_structure(S, nw, k, G, lane, U, sv, si, t, tc);
+      U = update_and_structure(S, nw, k, G, cell_off, lane, U, sv, si, t, tc);
       build_table(S, table, lane, t, tc, U);
     }
     __syncthreads();
@@ -1073,6 +1144,38 @@ __global__ void pack_kernel(MatDesc M, int group, int k, const uint8_t* assign, 
   }
 }
 
+// Keep a restart's outputs for the rows where it beat the best objective so far.  One
+// workgroup per row; every lane reads both objectives before lane 0 updates the best.
+__global__ void restart_merge_kernel(MergeDesc d) {
+  const int64_t row = blockIdx.x;
+  const double cand = d.cand_obj[row];
+  const bool take = cand < d.best_obj[row];  // NaN (a rejected row) is never taken
+  __syncthreads();
+  if (!take) return;
+  const int64_t nb = d.n_cols / 2;
+  for (int64_t i = threadIdx.x; i < nb; i += blockDim.x) d.codes[row * nb + i] = d.cand_codes[row * nb + i];
+  if (threadIdx.x < d.n_clusters) {
+    const int64_t j = row * d.n_clusters + threadIdx.x;
+    d.lut[j] = d.cand_lut[j];
+    if (d.c) d.c[j] = d.cand_c[j];
+    if (d.picks) d.picks[j] = d.cand_picks[j];
+  }
+  if (threadIdx.x == 0) d.best_obj[row] = cand;
+}
+
+template <int E, int NWMAX, int MODE>
+void launch_kernel(const LaunchArgs& args, dim3 grid, dim3 block, size_t smem, hipStream_t stream,
+                   bool wide, bool var) {
+  if (wide && var)
+    hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE, true, true>), grid, block, smem, stream, args);
+  else if (wide)
+    hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE, true, false>), grid, block, smem, stream, args);
+  else if (var)
+    hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE, false, true>), grid, block, smem, stream, args);
+  else
+    hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE, false, false>), grid, block, smem, stream, args);
+}
+
 template <int E, int NWMAX>
 hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream) {
   const int nw = (NWMAX == 1) ? 1 : args.nw;
@@ -1082,35 +1185,12 @@ hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipSt
   const dim3 grid(static_cast<unsigned>(n_blocks));
   const dim3 block(kWave * nw);
   const bool wide = args.group >= E;
+  const bool var = args.variant != 0 || args.restart != 0;
   switch (mode) {
-    case MODE_FULL:
-      if (wide)
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_FULL, true>), grid, block, smem, stream, args);
-      else
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_FULL, false>), grid, block, smem, stream,
-                           args);
-      break;
-    case MODE_SCALE:
-      if (wide)
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SCALE, true>), grid, block, smem, stream, args);
-      else
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SCALE, false>), grid, block, smem, stream,
-                           args);
-      break;
-    case MODE_SEED:
-      if (wide)
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SEED, true>), grid, block, smem, stream, args);
-      else
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_SEED, false>), grid, block, smem, stream,
-                           args);
-      break;
-    case MODE_STEP:
-      if (wide)
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_STEP, true>), grid, block, smem, stream, args);
-      else
-        hipLaunchKernelGGL((any4_rows_kernel<E, NWMAX, MODE_STEP, false>), grid, block, smem, stream,
-                           args);
-      break;
+    case MODE_FULL: launch_kernel<E, NWMAX, MODE_FULL>(args, grid, block, smem, stream, wide, var); break;
+    case MODE_SCALE: launch_kernel<E, NWMAX, MODE_SCALE>(args, grid, block, smem, stream, wide, var); break;
+    case MODE_SEED: launch_kernel<E, NWMAX, MODE_SEED>(args, grid, block, smem, stream, wide, var); break;
+    case MODE_STEP: launch_kernel<E, NWMAX, MODE_STEP>(args, grid, block, smem, stream, wide, var); break;
     default:
       return hipErrorInvalidValue;
   }
@@ -1148,6 +1228,13 @@ hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t 
     case 64: return launch_mode<64, 8>(args, mode, n_blocks, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t stream) {
+  if (d.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(restart_merge_kernel, dim3(static_cast<unsigned>(d.n_rows)), dim3(256), 0,
+                     stream, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {

@@ -38,6 +38,14 @@ struct MatDesc {
   int32_t* picks_out;
 };
 
+// Method variant word (any4_params.variant; 0 = the paper's defaults).
+constexpr int32_t kVarWeightMask = 0x3;       // sample weights: 0 alpha*E|x|, 1 E|x|, 2 none
+constexpr int32_t kVarInitShift = 2;          // init: 0 k-means++, 1 random, 2 uniform levels
+constexpr int32_t kVarSymmetric = 1 << 4;     // Eq. 3 scaling
+constexpr int32_t kVarRestartShift = 8;       // bits 8-15: restarts - 1
+constexpr int32_t kVarKnownBits = 0xFF1F;
+enum : int32_t { INIT_KMEANSPP = 0, INIT_RANDOM = 1, INIT_UNIFORM = 2 };
+
 struct LaunchArgs {
   MatDesc m[kMaxMats];
   int64_t row_start[kMaxMats + 1];  // block b belongs to matrix i when row_start[i] <= b < row_start[i+1]
@@ -46,9 +54,11 @@ struct LaunchArgs {
   int32_t n_clusters;
   int32_t iters;
   int32_t nw;                       // waves per row (one workgroup per row)
-  int32_t pad_;
+  int32_t variant;                  // method variant word (restart bits are handled by the host)
   uint64_t seed;
   uint32_t* status;                 // device status word or NULL
+  int32_t restart;                  // the Philox counter's second word is t + 16 * restart
+  int32_t pad_;
 };
 
 // Row-kernel launch geometry for a row length: elements per lane E and waves per row.
@@ -66,6 +76,26 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 // Emission-only kernel behind any4_stage_pack.
 hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_t* assign,
                        const float* c, const float* alpha, const float* beta, hipStream_t stream);
+
+// Restarts: after restart r has written its outputs to the `cand_*` buffers, keep them
+// for every row whose objective is below the best so far (the earlier restart wins ties).
+struct MergeDesc {
+  int64_t n_rows;
+  int64_t n_cols;
+  int32_t n_clusters;
+  int32_t pad_;
+  const uint8_t* cand_codes;
+  const uint16_t* cand_lut;
+  const double* cand_obj;
+  const float* cand_c;        // or NULL
+  const int32_t* cand_picks;  // or NULL
+  uint8_t* codes;
+  uint16_t* lut;
+  double* best_obj;
+  float* c;                   // or NULL
+  int32_t* picks;             // or NULL
+};
+hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t stream);
 
 // ---- bookends (any4_bookends.hip)
 
