@@ -72,6 +72,8 @@ def lib():
         L.oracle_act_absmean.restype = ctypes.c_int
         L.oracle_dequantize.argtypes = [P, P, P, P, i64, i64, i32, i32, P]
         L.oracle_dequantize.restype = ctypes.c_int
+        L.oracle_lut_gemv.argtypes = [P, P, P, P, i64, i64, i32, i32, P, i32, i64, P, P]
+        L.oracle_lut_gemv.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -147,6 +149,24 @@ def dequantize(codes, lut, scale, offset, group: int, n_clusters: int) -> np.nda
     if st != 0:
         raise ValueError("oracle_dequantize: invalid argument")
     return out
+
+
+def lut_gemv(codes, lut, scale, offset, group: int, n_clusters: int, x: np.ndarray, dtype: int):
+    """y [M, N] fp32 = x [M, K] times the dequantized weight transposed (fp64 sums), and the
+    magnitude scale s [M, N] (sum |x| (|alpha L| + |beta|)) for judging fp32 evaluations."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    lut, scale, offset = (np.ascontiguousarray(np.asarray(a).view(np.uint16)) for a in (lut, scale, offset))
+    x = np.ascontiguousarray(x)
+    assert x.dtype == (np.float32 if dtype == 0 else np.uint16) and x.ndim == 2
+    N, K = codes.shape[0], codes.shape[1] * 2
+    M = x.shape[0]
+    y = np.zeros((M, N), np.float32)
+    s = np.zeros((M, N), np.float64)
+    st = lib().oracle_lut_gemv(_p(codes), _p(lut), _p(scale), _p(offset), N, K, group, n_clusters,
+                               _p(x), dtype, M, _p(y), _p(s))
+    if st != 0:
+        raise ValueError("oracle_lut_gemv: invalid argument")
+    return y, s
 
 
 # --- row-level steps -------------------------------------------------------------

@@ -581,3 +581,41 @@ int oracle_dequantize(const uint8_t* codes, const uint16_t* lut, const uint16_t*
     }
     return ORACLE_OK;
 }
+
+/* LUT-dequantized matrix-vector products (the inference consumer of the emitted
+ * format; the paper's tinygemm kernels dequantize weights on the fly before the
+ * multiply, Section 4.2): y[m, i] = sum_j x[m, j] * w_hat[i, j], with w_hat the Eq. 4
+ * dequantization above (fp32) and x [M, K] fp32 or bf16 bits (dtype); each product is
+ * exact in fp64 and the sum runs in fp64 in column order; y [M, N] is that sum rounded
+ * to fp32.  Also returns, per output, the magnitude scale
+ * s[m, i] = sum_j |x[m, j]| * (|fl(alpha * LUT[q])| + |beta|) in fp64, against which a
+ * differently ordered fp32 evaluation is judged. */
+int oracle_lut_gemv(const uint8_t* codes, const uint16_t* lut, const uint16_t* scale,
+                    const uint16_t* offset, int64_t N, int64_t K, int32_t group, int32_t k,
+                    const void* x, int32_t dtype, int64_t M, float* y, double* s) {
+    if (M < 1 || N < 0 || K < 2 || (K & 1) || group < 1 || K % group != 0 || k < 1 || k > 16 ||
+        (dtype != 0 && dtype != 1))
+        return ORACLE_ERR_INVALID_ARG;
+    const int64_t G = K / group;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t i = 0; i < N; ++i) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < K; ++j) {
+                const uint8_t byte = codes[i * (K / 2) + j / 2];
+                const int q = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                const float level = q < k ? fp16_to_f32(lut[i * k + q]) : NAN;
+                const float alpha = fp16_to_f32(scale[i * G + j / group]);
+                const float beta = fp16_to_f32(offset[i * G + j / group]);
+                const float prod = alpha * level;
+                const float w = prod + beta;
+                const float xv = dtype == 0 ? ((const float*)x)[m * K + j]
+                                            : bf16_to_f32(((const uint16_t*)x)[m * K + j]);
+                acc += (double)xv * (double)w;
+                mag += fabs((double)xv) * (fabs((double)prod) + fabs((double)beta));
+            }
+            y[m * N + i] = (float)acc;
+            if (s) s[m * N + i] = mag;
+        }
+    }
+    return ORACLE_OK;
+}

@@ -182,3 +182,43 @@ def test_any4_output_error_below_int4_on_synthetic_activations():
     e4, ei = rel(w_any4), rel(w_int4)
     assert e4 < ei, (e4, ei)
     assert e4 < 0.2
+
+
+# --- LUT-dequantized matrix-vector products ----------------------------------------------
+
+def test_gemv_worked_example():
+    """The Eq. 4 example above (w_hat = [6.25, -0.75, 8, 3]) times x = [1, 2, -1, 0.5]:
+    6.25 - 1.5 - 8 + 1.5 = -1.75; a second token [0, 0, 0.25, 4] gives 2 + 12 = 14."""
+    codes = np.array([[0x13, 0x02]], np.uint8)
+    lut = np.array([[0x0000, 0x3C00, 0x4100, 0x4B80]], np.uint16)
+    scale = np.array([[0x3800, 0x4000]], np.uint16)
+    offset = np.array([[0xBD00, 0x4200]], np.uint16)
+    x = np.array([[1, 2, -1, 0.5], [0, 0, 0.25, 4]], np.float32)
+    y, s = oracle.lut_gemv(codes, lut, scale, offset, 2, 4, x, F32)
+    assert np.array_equal(y, np.array([[-1.75], [14.0]], np.float32))
+    # magnitude scale: sum |x| (|alpha L| + |beta|) = 1*8.75 + 2*1.75 + 1*8 + 0.5*3
+    assert s[0, 0] == 8.75 + 3.5 + 8 + 1.5
+
+
+def test_gemv_matches_dequantize_times_x():
+    m = make_matrix("gemv", 20, 512, BF16, 71)
+    out = oracle.quantize(m.w, BF16, m.act, 128, 16, 6)
+    w_hat = oracle.dequantize(out["codes"], out["lut"], out["scale"], out["offset"], 128, 16)
+    x = draw_activations(np.random.default_rng(72), 3, m.act, BF16)
+    y, _ = oracle.lut_gemv(out["codes"], out["lut"], out["scale"], out["offset"], 128, 16, x, BF16)
+    ref = _bf16_to_f32(x).astype(np.float64) @ w_hat.astype(np.float64).T   # numpy fp64 product
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-30)
+    assert y.shape == (3, 20)
+
+
+def test_gemv_is_linear_in_x():
+    m = make_matrix("lin", 6, 256, F32, 73)
+    out = oracle.quantize(m.w, F32, m.act, 64, 8, 4)
+    rng = np.random.default_rng(74)
+    x1 = (rng.integers(-8, 8, (2, 256)) * 0.25).astype(np.float32)   # sums stay exact
+    x2 = (rng.integers(-8, 8, (2, 256)) * 0.5).astype(np.float32)
+    args = (out["codes"], out["lut"], out["scale"], out["offset"], 64, 8)
+    y1, _ = oracle.lut_gemv(*args, x1, F32)
+    y2, _ = oracle.lut_gemv(*args, x2, F32)
+    y12, _ = oracle.lut_gemv(*args, x1 + x2, F32)
+    assert np.allclose(y12, y1 + y2, rtol=1e-6, atol=1e-6)
