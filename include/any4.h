@@ -213,6 +213,26 @@ int any4_act_absmean(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t n
 int any4_dequantize(const any4_matrix* m, const any4_params* params, void* w_out,
                     int32_t out_dtype, hipStream_t stream);
 
+/* The quantized matrix applied to a few tokens without materializing it (the inference
+ * consumer; the paper's tinygemm kernels dequantize on the fly before the multiply,
+ * Section 4.2): y[t, i] = sum_j x[t, j] * w_hat[i, j], w_hat the Eq. 4 dequantization
+ * of any4_dequantize, accumulated in fp32.
+ *   m       codes, lut, scale, offset as emitted (w, act_absmean, objective unused)
+ *   params  group and n_clusters of the codes (iters, seed, variant ignored)
+ *   x       [n_tokens, n_cols] activations, fp32 or bf16 bits (x_dtype)
+ *   y       out [n_tokens, n_rows] fp32
+ * Each 16-column block is evaluated as alpha * sum x*LUT[q] + beta * sum x; against an
+ * exact evaluation of the Eq. 4 definition the error stays within 1e-5 of
+ * sum_j |x_j| (|alpha*LUT[q_j]| + |beta|), and the summation order is fixed (repeated calls
+ * give identical bits).  Supports 1 <= n_tokens <= 8, n_cols and group multiples of 16,
+ * codes 8-byte and x 16-byte aligned (ANY4_ERR_UNSUPPORTED otherwise; use
+ * any4_dequantize and a GEMM for larger batches).  A code at or above n_clusters gives
+ * NaN.  Errors:
+ * ANY4_ERR_INVALID_ARG (NULL pointer, bad sizes or dtype), ANY4_ERR_UNSUPPORTED,
+ * ANY4_ERR_HIP. */
+int any4_lut_gemv(const any4_matrix* m, const any4_params* params, const void* x, int32_t x_dtype,
+                  int64_t n_tokens, float* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

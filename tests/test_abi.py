@@ -154,6 +154,33 @@ def test_bookends_validate_before_launch(L):
     assert L.any4_dequantize(ctypes.byref(m0), ctypes.byref(p), None, 1, None) == 0
 
 
+
+def test_lut_gemv_validates_before_launch(L):
+    """The LUT matrix-vector product rejects bad arguments, and reports shapes outside
+    its kernel (more than 8 tokens, K or group not a multiple of 16, codes not 8-byte or
+    x not 16-byte aligned) as unsupported, without a HIP call."""
+    p = any4.params(128, 16, 20, 0)
+    m = _mat()
+    y = 0x9000
+    gemv = L.any4_lut_gemv
+    assert gemv(ctypes.byref(m), ctypes.byref(p), None, 1, 1, y, None) == 1
+    assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7000, 1, 1, None, None) == 1
+    assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7000, 5, 1, y, None) == 1
+    assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7000, 1, 0, y, None) == 1
+    assert gemv(ctypes.byref(m), ctypes.byref(any4.params(96)), 0x7000, 1, 1, y, None) == 1
+    assert gemv(ctypes.byref(_mat(k=500)), ctypes.byref(p), 0x7000, 1, 1, y, None) == 1
+    assert gemv(None, ctypes.byref(p), 0x7000, 1, 1, y, None) == 1
+    assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7000, 1, 9, y, None) == 2
+    assert gemv(ctypes.byref(m), ctypes.byref(any4.params(8)), 0x7000, 1, 1, y, None) == 2
+    assert gemv(ctypes.byref(_mat(k=520)), ctypes.byref(any4.params(8)), 0x7000, 1, 1, y, None) == 2
+    odd = _mat()
+    odd.codes = 0x3004
+    assert gemv(ctypes.byref(odd), ctypes.byref(p), 0x7000, 1, 1, y, None) == 2
+    assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7008, 1, 1, y, None) == 2   # x alignment
+    m0 = any4.Any4Matrix()
+    m0.n_rows, m0.n_cols = 0, 256
+    assert gemv(ctypes.byref(m0), ctypes.byref(p), None, 1, 1, None, None) == 0
+
 def test_launch_geometry(L):
     assert any4.launch_geometry(4096) == (32, 2)
     assert any4.launch_geometry(512) == (8, 1)

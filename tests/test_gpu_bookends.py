@@ -5,6 +5,10 @@
     two can differ only in the last bit of the fp64 sum), bit-identical across runs.
   * dequantization (Section 2.5.2, Eq. 4): bit-exact in fp32 and in bf16 (RNE) on
     quantizer outputs and on random codes/LUTs/scales, vector and scalar paths.
+  * LUT matrix-vector products (Eq. 4 applied on the fly): within 1e-5 of
+    sum_j |x_j| (|alpha L| + |beta|) of the oracle's fp64 result, one to eight tokens,
+    one and several K-slices per row group, NaN where a code lies past the LUT,
+    bit-identical across calls.
   * end to end: E|x| from synthetic activations on the GPU -> quantize -> dequantize,
     exact reconstruction of exact-level rows, and any4's output error below uniform
     int4 with the same group scaling.
@@ -236,3 +240,85 @@ def test_dequant_full_up_proj_sampled_rows():
                             q.scale.cpu().numpy()[rows].view(np.uint16),
                             q.offset.cpu().numpy()[rows].view(np.uint16), w.group, w.n_clusters)
     assert np.array_equal(out[rows], oracle.bf16_bits(ref))
+
+
+# --- LUT-dequantized matrix-vector products -------------------------------------------------
+
+GEMV_TOL = 1e-5   # relative to sum_j |x_j| (|alpha L| + |beta|), the oracle's magnitude scale
+
+
+def _check_gemv(q, g, k, codes, lut, scale, offset, x, dtype, name):
+    got = any4().lut_gemv(q, _dev(x), g, k).cpu().numpy()
+    ref, s = oracle.lut_gemv(codes, lut, scale, offset, g, k, x, dtype)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), name
+    err = np.abs(got[~nan].astype(np.float64) - ref[~nan])
+    bound = GEMV_TOL * s[~nan] + 1e-30
+    assert np.all(err <= bound), (name, float((err / bound).max()))
+    return float((err / np.maximum(s[~nan], 1e-300)).max()) if err.size else 0.0
+
+
+# (name, N, K, group, k, M, x dtype, seed): one to eight tokens, one and several x slices
+GEMV_RANDOM = [
+    ("m1_k4096_bf16", 40, 4096, 128, 16, 1, BF16, 11),
+    ("m3_k512_f32", 33, 512, 64, 8, 3, F32, 12),
+    ("m5_k2048_bf16_g16", 17, 2048, 16, 16, 5, BF16, 13),
+    ("m8_k28672_bf16", 9, 28672, 128, 16, 8, BF16, 14),
+    ("m2_k6160_f32_codes_past_lut", 21, 6160, 16, 4, 2, F32, 15),
+]
+
+
+@pytest.mark.parametrize("case", GEMV_RANDOM, ids=[c[0] for c in GEMV_RANDOM])
+def test_gemv_random_fields(case):
+    name, N, K, g, k, M, dtype, seed = case
+    say(f"gemv {name}: N={N} K={K} M={M}")
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    codes &= np.uint8({16: 0xFF, 8: 0x77, 4: 0x33}[k])
+    if "past_lut" in name:
+        codes[::4, K // 3] |= np.uint8(0xC0)     # one code past the LUT on every 4th row
+    lut = (rng.standard_normal((N, k)) * 4).astype(np.float16).view(np.uint16)
+    scale = (rng.lognormal(-5, 1, (N, K // g))).astype(np.float16).view(np.uint16)
+    offset = (rng.standard_normal((N, K // g)) * 0.05).astype(np.float16).view(np.uint16)
+    x = draw_activations(rng, M, draw_act(rng, K), dtype)
+    q = any4().Quantized(codes=_dev(codes), lut=torch.from_numpy(lut.view(np.float16)).cuda(),
+                         scale=torch.from_numpy(scale.view(np.float16)).cuda(),
+                         offset=torch.from_numpy(offset.view(np.float16)).cuda(), objective=None)
+    worst = _check_gemv(q, g, k, codes, lut, scale, offset, x, dtype, name)
+    say(f"  {name}: worst error {worst:.2e} of the magnitude scale")
+    a = any4().lut_gemv(q, _dev(x), g, k).cpu().numpy()
+    b = any4().lut_gemv(q, _dev(x), g, k).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))      # fixed summation order
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_gemv_full_up_proj_sampled_rows(M):
+    """The quantized 14336 x 4096 up_proj times M calibration-like tokens (the launch
+    bench.py times), checked on 128 sampled rows."""
+    w = make("up_proj")
+    m = w.matrices[0]
+    wd, act = to_device(m)
+    q = any4().quantize(wd, act, w.group, w.n_clusters, w.iters)
+    x = draw_activations(np.random.default_rng(90 + M), M, m.act, BF16)
+    got = any4().lut_gemv(q, _dev(x), w.group, w.n_clusters).cpu().numpy()
+    rows = np.sort(np.random.default_rng(91).choice(m.w.shape[0], 128, replace=False))
+    ref, s = oracle.lut_gemv(q.codes.cpu().numpy()[rows], q.lut.cpu().numpy()[rows].view(np.uint16),
+                             q.scale.cpu().numpy()[rows].view(np.uint16),
+                             q.offset.cpu().numpy()[rows].view(np.uint16), w.group, w.n_clusters, x, BF16)
+    err = np.abs(got[:, rows].astype(np.float64) - ref)
+    assert np.all(err <= GEMV_TOL * s), float((err / s).max())
+    say(f"  up_proj M={M}: worst error {float((err / s).max()):.2e} of the magnitude scale")
+
+
+def test_gemv_unsupported_and_invalid():
+    q = any4().Quantized(codes=torch.zeros((4, 256), dtype=torch.uint8, device="cuda"),
+                         lut=torch.zeros((4, 16), dtype=torch.float16, device="cuda"),
+                         scale=torch.zeros((4, 4), dtype=torch.float16, device="cuda"),
+                         offset=torch.zeros((4, 4), dtype=torch.float16, device="cuda"),
+                         objective=None)
+    assert torch.equal(any4().lut_gemv(q, torch.ones((2, 512), device="cuda")),
+                       torch.zeros((2, 4), device="cuda"))
+    with pytest.raises(any4().Any4Error):
+        any4().lut_gemv(q, torch.ones((9, 512), device="cuda"))        # more than 8 tokens
+    with pytest.raises(any4().Any4Error):
+        any4().lut_gemv(q, torch.ones((1, 512), device="cuda"), group=8)  # group below 16

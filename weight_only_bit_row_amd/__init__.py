@@ -33,7 +33,7 @@ EXPORTED = [
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
     "any4_stage_full",
-    "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize",
+    "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize", "any4_lut_gemv",
 ]
 
 
@@ -98,6 +98,7 @@ def lib():
         L.any4_act_absmean.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P,
                                        ctypes.c_size_t, P]
         L.any4_dequantize.argtypes = [MP, PP, P, ctypes.c_int32, P]
+        L.any4_lut_gemv.argtypes = [MP, PP, P, ctypes.c_int32, ctypes.c_int64, P, P]
         for name in EXPORTED:
             if name != "any4_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -312,6 +313,30 @@ def dequantize(q: Quantized, group: int = 128, n_clusters: int = 16, out_dtype=N
     code = ANY4_BF16 if out_dtype == torch.bfloat16 else ANY4_F32
     _check(lib().any4_dequantize(ctypes.byref(m), ctypes.byref(p), _ptr(out), code,
                                  _stream(q.codes.device)), "any4_dequantize")
+    return out
+
+
+def lut_gemv(q: Quantized, x, group: int = 128, n_clusters: int = 16, out=None):
+    """y [M, N] fp32 = x [M, K] (bf16/fp32, M <= 8) times the dequantized weight,
+    transposed, without materializing it."""
+    torch = _torch()
+    _require_gpu(q.codes)
+    code, x = _dtype_code(x)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    N, K = int(q.codes.shape[0]), int(q.codes.shape[1]) * 2
+    M = int(x.shape[0])
+    if int(x.shape[1]) != K:
+        raise ValueError("x has the wrong number of columns")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=q.codes.device)
+    m = Any4Matrix()
+    m.n_rows, m.n_cols = N, K
+    m.w_dtype = ANY4_F32
+    m.codes, m.lut, m.scale, m.offset = _ptr(q.codes), _ptr(q.lut), _ptr(q.scale), _ptr(q.offset)
+    p = params(group, n_clusters, 0, 0)
+    _check(lib().any4_lut_gemv(ctypes.byref(m), ctypes.byref(p), _ptr(x), code, M, _ptr(out),
+                               _stream(q.codes.device)), "any4_lut_gemv")
     return out
 
 

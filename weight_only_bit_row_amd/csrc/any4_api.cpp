@@ -430,4 +430,39 @@ int any4_dequantize(const any4_matrix* m, const any4_params* params, void* w_out
   return any4::launch_dequant(d, stream) == hipSuccess ? ANY4_OK : ANY4_ERR_HIP;
 }
 
+int any4_lut_gemv(const any4_matrix* m, const any4_params* params, const void* x, int32_t x_dtype,
+                  int64_t n_tokens, float* y, hipStream_t stream) {
+  if (!m || !params) return ANY4_ERR_INVALID_ARG;
+  if (params->group < 2 || !is_pow2(params->group)) return ANY4_ERR_INVALID_ARG;
+  if (!(params->n_clusters == 2 || params->n_clusters == 4 || params->n_clusters == 8 ||
+        params->n_clusters == 16))
+    return ANY4_ERR_INVALID_ARG;
+  if (m->n_rows < 0 || m->n_cols < 2 || (m->n_cols & 1) || m->n_cols % params->group != 0)
+    return ANY4_ERR_INVALID_ARG;
+  if (x_dtype != ANY4_F32 && x_dtype != ANY4_BF16) return ANY4_ERR_INVALID_ARG;
+  if (n_tokens < 1) return ANY4_ERR_INVALID_ARG;
+  if (n_tokens > any4::kGemvMaxTokens || m->n_cols % 16 != 0 || params->group % 16 != 0)
+    return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows == 0) return ANY4_OK;
+  if (!m->codes || !m->lut || !m->scale || !m->offset || !x || !y) return ANY4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(m->codes) & 7) != 0 || (reinterpret_cast<uintptr_t>(x) & 15) != 0)
+    return ANY4_ERR_UNSUPPORTED;
+  any4::GemvDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.codes = m->codes;
+  d.lut = m->lut;
+  d.scale = m->scale;
+  d.offset = m->offset;
+  d.x = x;
+  d.y = y;
+  d.n_tokens = n_tokens;
+  d.n_rows = m->n_rows;
+  d.n_cols = m->n_cols;
+  d.group = params->group;
+  d.n_clusters = params->n_clusters;
+  d.x_bf16 = x_dtype == ANY4_BF16 ? 1 : 0;
+  return any4::launch_gemv(d, stream) == hipSuccess ? ANY4_OK : ANY4_ERR_HIP;
+}
+
 }  // extern "C"

@@ -297,6 +297,268 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
   }
 }
 
+// ---------------------------------------------------------------------------------
+// LUT-dequantized matrix-vector product for a few tokens (M <= 8), the consumer of the
+// emitted format (the paper's tinygemm dequantizes on the fly before its multiply):
+//   y[m][n] = sum_j x[m][j] * (alpha_{n,g(j)} * LUT_n[q_{n,j}] + beta_{n,g(j)}),
+// taken per 16-column chunk c of one group as alpha * (sum_{j in c} x_j L_{q_j}) +
+// beta * (sum_{j in c} x_j), all in fp32.  HBM-bound at decode sizes: the codes are
+// the only large operand (half a byte per weight), x is a few KB that every wave reads
+// through L1/L2.
+//
+// One wave owns R = 4 rows and one K-slice.  Lane l takes the 16-column chunks
+// l, l + 64, ... of the slice for all R rows, so each 8-byte code load is part of a
+// 512-byte contiguous run per row and each x value, converted once, serves R rows.
+// The row LUTs sit in LDS, 16 floats per row; a nibble's LDS address is formed by one
+// byte permute that drops 4*q (shifted and masked, four nibbles per register) into
+// byte 0 of the wave's 256-byte LUT block (the row offset is an immediate).  All lanes
+// of a wave look up the same row at a time: 16 consecutive words, no bank conflicts.  Partial sums of the R*MT
+// outputs are reduced across the wave by a butterfly that halves the values held per
+// lane at each step, and across the K-slices of a row group through LDS, in a fixed
+// order (the result does not depend on timing).
+constexpr int kGvWaves = 4;    // waves per workgroup
+
+template <int N>
+__device__ __forceinline__ float wave_reduce_spread(float (&v)[N], int lane) {
+  // On return, lanes whose low (6 - log2 N) bits are zero hold the wave total of value
+  // index lane >> (6 - log2 N).
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+  int o = 32;
+#pragma unroll
+  for (int h = N / 2; h >= 1; h /= 2, o /= 2) {
+    const bool up = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = up ? v[i] : v[i + h];
+      const float keep = up ? v[i + h] : v[i];
+      v[i] = keep + __shfl_xor(send, o);
+    }
+  }
+  float t = v[0];
+  for (; o >= 1; o /= 2) t += __shfl_xor(t, o);
+  return t;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
+  bf16x2 v;
+  __builtin_memcpy(&v, &u, 4);
+  return v;
+}
+
+// One chunk's weight data for the wave's R rows: codes, and the alpha/beta bits of the
+// chunk's group.
+template <int R>
+struct GvW {
+  uint2 cw[R];
+  uint16_t a[R], b[R];
+};
+
+// One chunk of x (16 columns of every token) as raw words, for prefetching.
+template <int MT, bool XBF>
+struct GvX {
+  uint32_t w[MT][XBF ? 8 : 16];
+};
+
+template <int MT, bool XBF>
+__device__ __forceinline__ void gv_load_x_raw(const GemvDesc& d, uint32_t col, GvX<MT, XBF>& x) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t base = (m < d.n_tokens ? m : d.n_tokens - 1) * d.n_cols;
+    const u32x4* p = XBF ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(d.x) + base + col)
+                         : reinterpret_cast<const u32x4*>(static_cast<const float*>(d.x) + base + col);
+#pragma unroll
+    for (int i = 0; i < (XBF ? 2 : 4); ++i) {
+      const u32x4 v = p[i];
+      x.w[m][4 * i] = v.x; x.w[m][4 * i + 1] = v.y; x.w[m][4 * i + 2] = v.z; x.w[m][4 * i + 3] = v.w;
+    }
+  }
+}
+
+// Rows per wave.  Four measured best at one and two tokens on 4096 x 14336 and
+// 14336 x 4096 (eight halves the wave count and hides less latency, two converts x for
+// fewer rows), and keeps the eight-token instance within the register file.
+template <int MT>
+constexpr int gv_rows() { return 4; }
+
+template <int MT, bool XBF>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int split_log2) {
+  constexpr int R = gv_rows<MT>();
+  constexpr int XW = MT <= 2 ? 8 : 4;   // x columns converted per step (register budget)
+  constexpr bool PX = MT <= 2;          // x of the next chunk prefetched with its codes (else
+                                        // this chunk's x is loaded with the next codes)
+  __shared__ __attribute__((aligned(1024))) float lut[kGvWaves][R][16];
+  __shared__ float part[kGvWaves][R * MT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int splits = 1 << split_log2;
+  const int ks = wave & (splits - 1);
+  const int64_t row0 =
+      ((int64_t(blockIdx.x) << (2 - split_log2)) + (wave >> split_log2)) * R;  // 4 waves per WG
+  const int64_t N = d.n_rows, K = d.n_cols;
+  const int gshift = __builtin_ctz(static_cast<uint32_t>(d.group));
+  const int64_t G = K >> gshift;
+  // the wave's LUT entries (16 per row) are fetched first and stored below
+  static_assert(R % 4 == 0, "R rows of 16 LUT entries are loaded 64 at a time");
+  uint16_t lut_bits[R / 4];
+#pragma unroll
+  for (int i = 0; i < R / 4; ++i) {
+    const int r = (lane >> 4) + 4 * i, q = lane & 15;
+    const bool ok = row0 + r < N && q < d.n_clusters;
+    lut_bits[i] = d.lut[ok ? (row0 + r) * d.n_clusters + q : 0];  // no branch
+  }
+  const uint8_t* codes[R];
+  const char* scale[R];
+  const char* offset[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = (row0 + r < N) ? row0 + r : N - 1;  // tail rows: read row N-1, never stored
+    codes[r] = d.codes + row * (K >> 1);
+    scale[r] = reinterpret_cast<const char*>(d.scale + row * G);
+    offset[r] = reinterpret_cast<const char*>(d.offset + row * G);
+  }
+  const uint32_t chunks = static_cast<uint32_t>(K >> 4);
+  const uint32_t per = (chunks + splits - 1) >> split_log2;
+  const uint32_t c_begin = ks * per;
+  const uint32_t c_end = c_begin + per < chunks ? c_begin + per : chunks;
+  const uint32_t c_last = c_end > c_begin ? c_end - 1 : c_begin;  // clamp for prefetches
+  auto load_w = [&](GvW<R>& w, uint32_t c) {
+    const uint32_t gb = ((c << 4) >> gshift) << 1;  // byte offset of the group's alpha/beta
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w.cw[r] = *reinterpret_cast<const uint2*>(codes[r] + (c << 3));
+      w.a[r] = *reinterpret_cast<const uint16_t*>(scale[r] + gb);
+      w.b[r] = *reinterpret_cast<const uint16_t*>(offset[r] + gb);
+    }
+  };
+  uint32_t c = c_begin + lane;
+  GvW<R> wcur;
+  GvX<MT, XBF> xcur;
+  load_w(wcur, c < c_last ? c : c_last);
+  if constexpr (PX) gv_load_x_raw<MT, XBF>(d, (c < c_last ? c : c_last) << 4, xcur);
+#pragma unroll
+  for (int i = 0; i < R / 4; ++i) {
+    const int r = (lane >> 4) + 4 * i, q = lane & 15;
+    lut[wave][r][q] = (row0 + r < N && q < d.n_clusters) ? half_bits_to_float(lut_bits[i])
+                                                          : __builtin_nanf("");
+  }
+  // each wave reads only its own LUT block; LDS operations of a wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // byte 0 of a LUT address comes from the codes, bytes 1..3 from the wave's block
+  const uint32_t block = static_cast<uint32_t>(wave) * (R * 64u);
+  const char* lut_bytes = reinterpret_cast<const char*>(&lut[0][0][0]);
+  float y[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) y[r][m] = 0.0f;
+
+  for (; c < c_end; c += 64) {
+    const uint32_t cn = c + 64 < c_last ? c + 64 : c_last;
+    GvW<R> wnext;
+    GvX<MT, XBF> xnext;
+    load_w(wnext, cn);
+    if constexpr (PX)
+      gv_load_x_raw<MT, XBF>(d, cn << 4, xnext);
+    else
+      gv_load_x_raw<MT, XBF>(d, c << 4, xcur);  // this chunk's x, issued with the next codes
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads go out before this one's math
+    float acc[R][MT], xs[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      xs[m] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][m] = 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // the two 8-nibble words of the chunk
+      uint32_t lo4[R], hi4[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w = h ? wcur.cw[r].y : wcur.cw[r].x;
+        lo4[r] = (w << 2) & 0x3C3C3C3Cu;   // 4 * nibbles 0, 2, 4, 6
+        hi4[r] = (w >> 2) & 0x3C3C3C3Cu;   // 4 * nibbles 1, 3, 5, 7
+      }
+#pragma unroll
+      for (int qq = 0; qq < 8 / XW; ++qq) {  // XW columns of x at a time
+        const int e0 = 8 * h + XW * qq;      // first column of this step within the chunk
+        float xv[MT][XW];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int e = 0; e < XW; ++e) {
+            const int j = e0 + e;
+            xv[m][e] = XBF ? ((j & 1) ? bf16_hi(xcur.w[m][j >> 1]) : bf16_lo(xcur.w[m][j >> 1]))
+                           : __uint_as_float(xcur.w[m][j]);
+          }
+        if constexpr (XBF) {
+          // sum of a bf16 pair in one dot product with (1, 1): exact products, fp32 sum
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < XW; e += 2)
+              xs[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xcur.w[m][(e0 + e) >> 1]),
+                                                      as_bf16x2(0x3F803F80u), xs[m], false);
+        } else {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < XW; ++e) xs[m] += xv[m][e];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int jj = 0; jj < XW / 2; ++jj) {
+            const uint32_t sel = 0x07060500u | uint32_t(jj + (XW / 2) * qq);
+            const float le = *reinterpret_cast<const float*>(
+                lut_bytes + __builtin_amdgcn_perm(block, lo4[r], sel) + r * 64);
+            const float lo = *reinterpret_cast<const float*>(
+                lut_bytes + __builtin_amdgcn_perm(block, hi4[r], sel) + r * 64);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              acc[r][m] = fmaf(xv[m][2 * jj], le, acc[r][m]);
+              acc[r][m] = fmaf(xv[m][2 * jj + 1], lo, acc[r][m]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // fp16 alpha/beta feed mixed-precision multiply-adds (exact widening)
+      const float al = half_bits_to_float(wcur.a[r]), be = half_bits_to_float(wcur.b[r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) y[r][m] = fmaf(be, xs[m], fmaf(al, acc[r][m], y[r][m]));
+    }
+    wcur = wnext;
+    if constexpr (PX) xcur = xnext;
+  }
+
+  constexpr int NV = R * MT;
+  constexpr int kLow = (NV >= 64) ? 1 : 64 / NV;  // lanes per reduced value
+  float v[NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[r * MT + m] = y[r][m];
+  const float t = wave_reduce_spread<NV>(v, lane);
+  const int idx = lane / kLow;
+  const bool holder = (lane % kLow) == 0;
+  if (splits > 1) {
+    if (holder) part[wave][idx] = t;
+    __syncthreads();
+    if (ks != 0 || lane >= NV) return;
+    float s = part[wave][lane];
+    for (int k = 1; k < splits; ++k) s += part[wave + k][lane];
+    const int r = lane / MT, m = lane % MT;
+    if (row0 + r < N && m < d.n_tokens) d.y[m * N + row0 + r] = s;
+  } else if (holder) {
+    const int r = idx / MT, m = idx % MT;
+    if (row0 + r < N && m < d.n_tokens) d.y[m * N + row0 + r] = t;
+  }
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
@@ -339,6 +601,37 @@ hipError_t launch_absmean(const void* x, int dtype, int64_t n_tokens, int64_t n_
   hipLaunchKernelGGL(absmean_finish_kernel, dim3(static_cast<uint32_t>((n_cols + 63) / 64)),
                      dim3(kThreads), 0, stream, partial, plan.n_splits, n_tokens, n_cols, out);
   return hipGetLastError();
+}
+
+int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave) {
+  // split K over up to 4 waves of a workgroup while the grid holds fewer than 2048
+  // waves (8 per CU) and every lane keeps at least two chunks of its slice
+  const int64_t groups = (n_rows + rows_per_wave - 1) / rows_per_wave, chunks = n_cols / 16;
+  int l = 0;
+  while ((1 << l) < kGvWaves && groups << l < 2048 && chunks >> (l + 1) >= 128) ++l;
+  return l;
+}
+
+template <int MT>
+hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
+  constexpr int R = gv_rows<MT>();
+  const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R);
+  const int64_t groups = (d.n_rows + R - 1) / R;
+  const int64_t per_wg = kGvWaves >> l;
+  const dim3 grid(static_cast<uint32_t>((groups + per_wg - 1) / per_wg));
+  if (d.x_bf16)
+    hipLaunchKernelGGL((gemv_kernel<MT, true>), grid, dim3(kThreads), 0, stream, d, l);
+  else
+    hipLaunchKernelGGL((gemv_kernel<MT, false>), grid, dim3(kThreads), 0, stream, d, l);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
+  if (d.n_rows == 0) return hipSuccess;
+  if (d.n_tokens <= 1) return launch_gemv_mt<1>(d, stream);
+  if (d.n_tokens <= 2) return launch_gemv_mt<2>(d, stream);
+  if (d.n_tokens <= 4) return launch_gemv_mt<4>(d, stream);
+  return launch_gemv_mt<8>(d, stream);
 }
 
 hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream) {

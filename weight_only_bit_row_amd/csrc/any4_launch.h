@@ -125,4 +125,23 @@ struct DequantDesc {
 };
 hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream);
 
+// y [M, N] fp32 = x [M, K] times the Eq. 4 dequantized weight, transposed (M <= 8).
+struct GemvDesc {
+  const uint8_t* codes;
+  const uint16_t* lut;
+  const uint16_t* scale;
+  const uint16_t* offset;
+  const void* x;
+  float* y;
+  int64_t n_tokens;          // M
+  int64_t n_rows;            // N
+  int64_t n_cols;            // K
+  int32_t group;
+  int32_t n_clusters;
+  int32_t x_bf16;            // 0: fp32 x, 1: bf16 bits
+  int32_t pad_;
+};
+constexpr int kGemvMaxTokens = 8;
+hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream);
+
 }  // namespace any4
