@@ -111,8 +111,10 @@ def copy_calibration():
 
 
 def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
-    """E|x| of a calibration batch and the Eq. 4 dequantization of the quantized matrix,
-    each timed over a batch of launches with HIP events on the launch stream."""
+    """E|x| of a calibration batch, the Eq. 4 dequantization of the quantized matrix and
+    its LUT matrix-vector product with one and eight tokens, each timed over a batch of
+    launches with HIP events on the launch stream (torch's bf16 product with the
+    dequantized matrix is timed beside the LUT product as a point of comparison)."""
     from workloads import CALIB, make_activations
 
     x_np = make_activations("calib_32x2048")
@@ -122,6 +124,9 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     act_out = torch.empty((Kx,), dtype=torch.float32, device=dev)
     ws = torch.empty((any4.act_absmean_workspace_bytes(T, Kx),), dtype=torch.uint8, device=dev)
     w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    x1, x8 = x[:1].contiguous(), x[:8].contiguous()     # decode tokens from the same batch
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    y8 = torch.empty((8, N), dtype=torch.float32, device=dev)
 
     def run_abs():
         any4.act_absmean(x, out=act_out, ws=ws)
@@ -129,10 +134,18 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     def run_dq():
         any4.dequantize(q, g, k, out=w_hat)
 
+    def run_gv1():
+        any4.lut_gemv(q, x1, g, k, out=y1)
+
+    def run_gv8():
+        any4.lut_gemv(q, x8, g, k, out=y8)
+
     if profile_steps:
         for _ in range(profile_steps):
             run_abs()
             run_dq()
+            run_gv1()
+            run_gv8()
         torch.cuda.synchronize()
         return None
 
@@ -150,8 +163,17 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
 
     ms_abs = per_launch_ms(run_abs, 20)
     ms_dq = per_launch_ms(run_dq, 100)
+    ms_gv1 = per_launch_ms(run_gv1, 200)
+    ms_gv8 = per_launch_ms(run_gv8, 100)
+    run_dq()
+    ms_mm1 = per_launch_ms(lambda: torch.nn.functional.linear(x1, w_hat), 200)
+    ms_mm8 = per_launch_ms(lambda: torch.nn.functional.linear(x8, w_hat), 100)
     bytes_abs = T * Kx * 2 + Kx * 4                      # read x once, write E|x|
-    bytes_dq = N * K // 2 + N * k * 2 + 2 * N * (K // g) * 2 + N * K * 2   # codes, LUT, alpha/beta; bf16 out
+    bytes_w = N * K // 2 + N * k * 2 + 2 * N * (K // g) * 2     # codes, LUT, alpha/beta
+    bytes_dq = bytes_w + N * K * 2                                # + bf16 out
+
+    def bytes_gv(M):
+        return bytes_w + M * K * 2 + M * N * 4                    # + bf16 x, fp32 y
 
     def roof(nbytes, ms, key):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -169,6 +191,14 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
          "workload": f"Eq. 4 dequantization of the quantized {N}x{K} up_proj (group {g}, "
                      f"{k} clusters) to bf16",
          "ms_per_call": ms_dq, "roofline": roof(bytes_dq, ms_dq, "dequant_traffic_bytes_per_launch")},
+        {"kernel": "any4_lut_gemv (gemv_kernel<1, bf16 x>)",
+         "workload": f"one calibration token times the quantized {N}x{K} up_proj, fp32 out",
+         "ms_per_call": ms_gv1, "bf16_matmul_ms_per_call": ms_mm1,
+         "roofline": roof(bytes_gv(1), ms_gv1, "gemv1_traffic_bytes_per_launch")},
+        {"kernel": "any4_lut_gemv (gemv_kernel<8, bf16 x>)",
+         "workload": f"eight calibration tokens times the quantized {N}x{K} up_proj, fp32 out",
+         "ms_per_call": ms_gv8, "bf16_matmul_ms_per_call": ms_mm8,
+         "roofline": roof(bytes_gv(8), ms_gv8, "gemv8_traffic_bytes_per_launch")},
     ]
 
 
@@ -183,9 +213,10 @@ def main():
                     help="Lloyd rounds for --profile-steps runs (default: the workload's 20)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-bookends", action="store_true", help="skip the E|x| and dequant kernels")
+    ap.add_argument("--no-bookends", action="store_true",
+                    help="skip the E|x|, dequant and LUT matrix-vector kernels")
     ap.add_argument("--bookends-only", action="store_true",
-                    help="with --profile-steps: run only the E|x| and dequant kernels")
+                    help="with --profile-steps: run only the E|x|, dequant and LUT matrix-vector kernels")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
