@@ -47,6 +47,8 @@ def lib():
         L.oracle_weights_row.argtypes = [P, P, i64, i32, P]
         L.oracle_weights_row.restype = ctypes.c_int
         L.oracle_seed_row.argtypes = [P, P, i64, i32, u64, u64, u32, P, P]
+        L.oracle_greedy_trials.argtypes = [i32]
+        L.oracle_greedy_trials.restype = i32
         L.oracle_seed_row.restype = ctypes.c_int
         L.oracle_estep_row.argtypes = [P, i64, P, i32, P]
         L.oracle_mstep_row.argtypes = [P, P, P, i64, P, i32, P]
@@ -173,9 +175,14 @@ def lut_gemv(codes, lut, scale, offset, group: int, n_clusters: int, x: np.ndarr
 
 # variant word (the paper's ablations; 0 = defaults): bits 0-1 sample weights
 # (0 alpha*E|x|, 1 E|x|, 2 none), bits 2-3 initialization (0 k-means++, 1 random,
-# 2 uniform levels), bit 4 symmetric scaling, bits 8-15 restarts - 1
+# 2 uniform levels, 3 greedy k-means++), bit 4 symmetric scaling, bits 8-15 restarts - 1
 WEIGHT_ALPHA_ACT, WEIGHT_ACT, WEIGHT_NONE = 0, 1, 2
-INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM = 0, 1 << 2, 2 << 2
+INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM, INIT_GREEDY = 0, 1 << 2, 2 << 2, 3 << 2
+
+
+def greedy_trials(n_clusters: int) -> int:
+    """Candidates per greedy k-means++ draw (2 + floor(ln k))."""
+    return int(lib().oracle_greedy_trials(n_clusters))
 SYMMETRIC = 1 << 4
 
 
@@ -204,8 +211,8 @@ def weights_row(alpha, act, group: int, weighting: int = 0):
 
 def seed_row(ws, a, n_clusters: int, seed: int = 0, row_id: int = 0, matrix_index: int = 0,
              init: int = 0, restart: int = 0, level0: float = 0.0):
-    """Initial centres; init 0 k-means++, 1 random, 2 uniform levels (plain codes, not
-    the shifted variant bits)."""
+    """Initial centres; init 0 k-means++, 1 random, 2 uniform levels, 3 greedy k-means++
+    (plain codes, not the shifted variant bits)."""
     ws, a = _f32(ws), _f32(a)
     c0 = np.zeros(n_clusters, np.float32)
     picks = np.zeros(n_clusters, np.int32)

@@ -242,8 +242,39 @@ static float sqdist(float x, float c) {
  *   init 2  uniform: the integer levels, c_t = level0 + t (int4's -7..8 up to the
  *           translation of the scaled domain: level0 = 0 for asymmetric scaling,
  *           1 - k/2 for symmetric); no draws, picks = -1.
+ *   init 3  greedy k-means++ (the variant scikit-learn runs by default): the first centre
+ *           as in k-means++; each later draw takes L = 2 + floor(ln k) candidates from
+ *           the same D^2 distribution (candidate s from Philox counter word
+ *           t + 16 * restart + 65536 * s, so candidate 0 is the plain draw) and keeps the
+ *           one whose potential, sum_j floor(a_j * min(D_j, (w_S_j - c)^2) * 2^(40-e))
+ *           with e of this draw, is smallest (the lowest s on equal potentials).  The
+ *           potentials are integers, so they compare exactly.
  * `restart` selects an independent draw stream for restarts: the Philox counter's
  * second word is t + 16 * restart. */
+
+/* Candidates per greedy draw: 2 + floor(ln k) for k = 2, 4, 8, 16. */
+int32_t oracle_greedy_trials(int32_t k) {
+    return 2 + (int32_t)floor(log((double)k));
+}
+
+/* The index whose prefix sum of q first exceeds r (the last index if none does). */
+static int64_t first_crossing(const uint64_t* q, int64_t K, uint64_t r) {
+    uint64_t prefix = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        prefix += q[j];
+        if (prefix > r) return j;
+    }
+    return K - 1;
+}
+
+static uint64_t philox_u64(uint64_t seed, uint64_t row_id, uint32_t word1, uint32_t matrix_index) {
+    uint32_t ctr[4] = {(uint32_t)row_id, word1, matrix_index, (uint32_t)(row_id >> 32)};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t x[4];
+    oracle_philox4x32_10(ctr, key, x);
+    return ((uint64_t)x[1] << 32) | (uint64_t)x[0];
+}
+
 int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
                          uint64_t seed, uint64_t row_id, uint32_t matrix_index,
                          int32_t init, int32_t restart, float level0,
@@ -282,18 +313,33 @@ int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
                 q[j] = (uint64_t)floor(v);
                 Q += q[j];
             }
-            uint32_t ctr[4] = {(uint32_t)row_id, (uint32_t)(t + 16 * restart), matrix_index,
-                               (uint32_t)(row_id >> 32)};
-            uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-            uint32_t x[4];
-            oracle_philox4x32_10(ctr, key, x);
-            uint64_t u = ((uint64_t)x[1] << 32) | (uint64_t)x[0];
+            const uint32_t word1 = (uint32_t)(t + 16 * restart);
+            uint64_t u = philox_u64(seed, row_id, word1, matrix_index);
             uint64_t r = (uint64_t)(((unsigned __int128)u * (unsigned __int128)Q) >> 64);
-            uint64_t prefix = 0;
-            int64_t pick = K - 1;
-            for (int64_t j = 0; j < K; ++j) {
-                prefix += q[j];
-                if (prefix > r) { pick = j; break; }
+            int64_t pick = first_crossing(q, K, r);
+            if (init == 3 && t > 0) {
+                /* greedy: more candidates, keep the one with the smallest potential */
+                const double sc = ldexp(1.0, 40 - e);
+                uint64_t best_pot = 0;
+                for (int32_t s = 0; s < oracle_greedy_trials(k); ++s) {
+                    int64_t cand = pick;
+                    if (s > 0) {
+                        uint64_t us = philox_u64(seed, row_id, word1 + 65536u * (uint32_t)s,
+                                                 matrix_index);
+                        uint64_t rs = (uint64_t)(((unsigned __int128)us * (unsigned __int128)Q) >> 64);
+                        cand = first_crossing(q, K, rs);
+                    }
+                    uint64_t pot = 0;
+                    for (int64_t j = 0; j < K; ++j) {
+                        float d = sqdist(ws[j], ws[cand]);
+                        float m = d < D[j] ? d : D[j];
+                        pot += (uint64_t)floor((double)(a[j] * m) * sc);
+                    }
+                    if (s == 0 || pot < best_pot) {
+                        best_pot = pot;
+                        if (s > 0) pick = cand;
+                    }
+                }
             }
             c0[t] = ws[pick];
             picks[t] = (int32_t)pick;
@@ -401,7 +447,7 @@ int oracle_any4_quantize_v(const void* w, int32_t dtype, int64_t n_rows, int64_t
     const int32_t restarts = ((variant >> 8) & 0xFF) + 1;
     if (n_rows < 0 || K < 2 || (K & 1) || group < 1 || K % group != 0 || iters < 0 ||
         (dtype != 0 && dtype != 1) || row_offset < 0 ||
-        !(k == 2 || k == 4 || k == 8 || k == 16) || weighting == 3 || init == 3 ||
+        !(k == 2 || k == 4 || k == 8 || k == 16) || weighting == 3 ||
         (variant & ~0xFF1F) != 0)
         return ORACLE_ERR_INVALID_ARG;
     const int32_t qr = k - 1;

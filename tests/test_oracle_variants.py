@@ -10,7 +10,12 @@ Numeric Representation for LLMs").
     not depend on E|x|, and equals E|x| weighting with a constant power-of-two E|x|.
   * initialization (Appendix C.2): uniform levels with no Lloyd round give the nearest
     integer level (the lower one on exact halves); random init draws each element with
-    probability proportional to a_j, never twice (chi-square over many Philox keys).
+    probability proportional to a_j, never twice (chi-square over many Philox keys);
+    greedy k-means++ (scikit-learn's default seeding) keeps the best of 2 + floor(ln k)
+    D^2 candidates: on a three-point row the worse second centre survives only when every
+    candidate is the worse one (probability 0.1^L instead of 0.1), its first centre and
+    first candidate are the plain draw, so its potential after two centres is never above
+    plain k-means++'s, and over real-like rows its final seeding potential is lower.
   * restarts: the kept objective is the minimum over the single restarts, whose
     centroids it reproduces, and one restart is the default path bit for bit.
 """
@@ -18,7 +23,8 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import (INIT_RANDOM, INIT_UNIFORM, SYMMETRIC, WEIGHT_ACT, WEIGHT_NONE, restarts)
+from oracle import (INIT_GREEDY, INIT_RANDOM, INIT_UNIFORM, SYMMETRIC, WEIGHT_ACT, WEIGHT_NONE,
+                    restarts)
 from workloads import BF16, F32, make_matrix
 
 
@@ -156,6 +162,80 @@ def test_random_init_all_weights_used_then_copies():
     assert np.all(c0[2:] == c0[0])
 
 
+def _binom_ok(hits, n, p, z=4.0):
+    mu = n * p
+    return abs(hits - mu) <= z * np.sqrt(n * p * (1 - p)) + 1
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_greedy_keeps_the_best_candidate(k):
+    """Row [0, 1, 3], unit weights.  After a first centre at 0, D = [0, 1, 9]: a D^2 draw
+    gives 1 with probability 0.1 and 3 with 0.9; centre 1 leaves potential 4, centre 3
+    leaves 1.  Greedy seeding keeps 1 only if all its L candidates are 1 (0.1^L, L = 2
+    for k = 2 and 3 for k = 4); plain seeding keeps it with probability 0.1."""
+    x = np.array([0, 1, 3], np.float32)
+    a = np.ones(3, np.float32)
+    L = oracle.greedy_trials(k)
+    assert L == {2: 2, 4: 3}[k]
+    n_first0 = {0: 0, 3: 0}
+    worse = {0: 0, 3: 0}
+    for s in range(9000):
+        plain = oracle.seed_row(x, a, k, seed=s, init=0)[1]
+        greedy = oracle.seed_row(x, a, k, seed=s, init=3)[1]
+        assert plain[0] == greedy[0]                   # the first centre is the plain draw
+        for init, p in ((0, plain), (3, greedy)):
+            if p[0] == 0:
+                n_first0[init] += 1
+                worse[init] += int(p[1] == 1)
+    assert _binom_ok(worse[0], n_first0[0], 0.1)
+    assert _binom_ok(worse[3], n_first0[3], 0.1 ** L)
+    assert worse[3] < worse[0] / 4
+
+
+def _potential(ws, a, centres):
+    d = (ws.astype(np.float64)[:, None] - centres.astype(np.float64)[None, :]) ** 2
+    return float((a.astype(np.float64) * d.min(axis=1)).sum())
+
+
+def test_greedy_never_worse_after_two_centres():
+    """With k = 2 the greedy draw at t = 1 includes the plain draw as its first
+    candidate and keeps the candidate of smallest potential, so its potential is never
+    above plain k-means++'s (fp64 potentials; the exact integer ones order the same up
+    to the 2^-40 quantization)."""
+    m = make_matrix("greedy2", 40, 512, F32, 68)
+    for i in range(40):
+        ws, al, _, _ = oracle.scale_row(m.w[i], 128, 2)
+        a, _ = oracle.weights_row(al, m.act, 128)
+        for s in range(5):
+            cp, pp = oracle.seed_row(ws, a, 2, seed=s, row_id=i, init=0)
+            cg, pg = oracle.seed_row(ws, a, 2, seed=s, row_id=i, init=3)
+            assert pp[0] == pg[0]
+            assert _potential(ws, a, cg) <= _potential(ws, a, cp) * (1 + 1e-9)
+
+
+def test_greedy_lowers_the_seeding_potential():
+    m = make_matrix("greedy16", 24, 1024, BF16, 69)
+    pot = {0: [], 3: []}
+    for i in range(24):
+        w32 = (m.w[i].astype(np.uint32) << 16).view(np.float32)
+        ws, al, _, _ = oracle.scale_row(w32, 128, 16)
+        a, _ = oracle.weights_row(al, m.act, 128)
+        for init in (0, 3):
+            c0, _ = oracle.seed_row(ws, a, 16, seed=7, row_id=i, init=init)
+            pot[init].append(_potential(ws, a, c0))
+    pg, pp = np.array(pot[3]), np.array(pot[0])
+    assert pg.mean() < 0.9 * pp.mean()
+    assert np.mean(pg < pp) > 0.7
+
+
+def test_greedy_variant_end_to_end_status():
+    m = make_matrix("greedyq", 4, 512, BF16, 70)
+    out = oracle.quantize(m.w, BF16, m.act, 128, 16, 6, variant=INIT_GREEDY)
+    assert out["status"] == 0
+    plain = oracle.quantize(m.w, BF16, m.act, 128, 16, 6)
+    assert np.array_equal(out["picks"][:, 0], plain["picks"][:, 0])
+
+
 # --- restarts ------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("init", [0, INIT_RANDOM])
@@ -187,5 +267,5 @@ def test_restarts_keep_the_lowest_objective(init):
 def test_variant_validation():
     w = np.zeros((1, 8), np.float32)
     act = np.ones(8, np.float32)
-    for v in (3, 3 << 2, 1 << 5, 1 << 16):
+    for v in (3, 1 << 5, 1 << 16):
         assert oracle.quantize(w, F32, act, 4, 4, 1, variant=v)["status"] == 1
