@@ -90,8 +90,12 @@ enum {
   /* initialization (Appendix C.2, Table A4): k-means++ (default); random: k distinct
    * elements drawn one after another with probability proportional to the sample
    * weight (the same Philox stream); uniform: the integer levels (0..2^n-1, or
-   * 1-2^(n-1)..2^(n-1) under symmetric scaling, i.e. int4's -7..8) */
+   * 1-2^(n-1)..2^(n-1) under symmetric scaling, i.e. int4's -7..8); greedy k-means++
+   * (scikit-learn's default form): every centre after the first keeps the best of
+   * 2 + floor(ln n_clusters) D^2 candidates (candidate s from Philox counter word
+   * t + 16 r + 65536 s), judged by the exact integer potential of the sampling step */
   ANY4_INIT_KMEANSPP = 0, ANY4_INIT_RANDOM = 1 << 2, ANY4_INIT_UNIFORM = 2 << 2,
+  ANY4_INIT_GREEDY = 3 << 2,
   /* symmetric scaling (Section 2.5.1, Eq. 3): alpha = max|w| / 2^(n-1), beta = 0 */
   ANY4_SCALE_SYMMETRIC = 1 << 4
 };

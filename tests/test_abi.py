@@ -91,10 +91,10 @@ def test_workspace_query_and_validation(L):
         st, _ = _ws_bytes(L, _mat(**mkw), any4.params(**kw))
         assert st == 1, (mkw, pkw)
     # variant word: unknown bits and unlisted field values are rejected
-    for v in (3, 3 << 2, 1 << 5, 1 << 16, -1):
+    for v in (3, 1 << 5, 1 << 16, -1):
         assert _ws_bytes(L, _mat(), any4.params(128, 16, 20, 0, v))[0] == 1, v
     for v in (any4.WEIGHT_ACT, any4.WEIGHT_NONE | any4.INIT_RANDOM, any4.SCALE_SYMMETRIC,
-              any4.INIT_UNIFORM | any4.SCALE_SYMMETRIC):
+              any4.INIT_UNIFORM | any4.SCALE_SYMMETRIC, any4.INIT_GREEDY):
         assert _ws_bytes(L, _mat(), any4.params(128, 16, 20, 0, v)) == (0, 256), v
     # restarts need room for one candidate set of outputs per matrix
     st, nbytes = _ws_bytes(L, _mat(n=4, k=512), any4.params(128, 16, 20, 0, any4.RESTARTS(3)))

@@ -25,7 +25,7 @@ def any4():
 
 
 W_ACT, W_NONE = 1, 2
-I_RANDOM, I_UNIFORM = 1 << 2, 2 << 2
+I_RANDOM, I_UNIFORM, I_GREEDY = 1 << 2, 2 << 2, 3 << 2
 SYM = 1 << 4
 
 VARIANTS = [
@@ -36,6 +36,8 @@ VARIANTS = [
     ("symmetric", SYM),
     ("symmetric_uniform", SYM | I_UNIFORM),
     ("symmetric_random_act", SYM | I_RANDOM | W_ACT),
+    ("init_greedy", I_GREEDY),
+    ("symmetric_greedy_none", SYM | I_GREEDY | W_NONE),
 ]
 
 # (name, N, K, dtype, group, n_clusters, seed): wide and narrow groups, any2, seven waves
@@ -138,7 +140,7 @@ def test_variant_end_to_end(case):
     _end_to_end(name, m, g, k, variant)
 
 
-@pytest.mark.parametrize("init", [0, I_RANDOM])
+@pytest.mark.parametrize("init", [0, I_RANDOM, I_GREEDY])
 def test_restarts_end_to_end(init):
     m = make_matrix("restarts", 16, 4096, BF16, 205)
     say(f"restarts init={init}")

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libany4.so")
 ANY4_F32, ANY4_BF16 = 0, 1
 # method variants (include/any4.h): OR them into `variant`
 WEIGHT_ALPHA_ACT, WEIGHT_ACT, WEIGHT_NONE = 0, 1, 2
-INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM = 0, 1 << 2, 2 << 2
+INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM, INIT_GREEDY = 0, 1 << 2, 2 << 2, 3 << 2
 SCALE_SYMMETRIC = 1 << 4
 
 

@@ -29,7 +29,6 @@ int check_params(const any4_params* p) {
   if (p->iters < 0) return ANY4_ERR_INVALID_ARG;
   if ((p->variant & ~any4::kVarKnownBits) != 0) return ANY4_ERR_INVALID_ARG;
   if ((p->variant & any4::kVarWeightMask) == 3) return ANY4_ERR_INVALID_ARG;
-  if (((p->variant >> any4::kVarInitShift) & 3) == 3) return ANY4_ERR_INVALID_ARG;
   return ANY4_OK;
 }
 

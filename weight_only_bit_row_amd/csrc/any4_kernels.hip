@@ -67,13 +67,25 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 
 // ---------------------------------------------------------------------------------
 // Shared memory: a fixed header, then per-wave lane-private bins [nw][2][16][64] fp64.
+// greedy k-means++: candidates per draw, 2 + floor(ln k) (2, 3, 4, 4 for k = 2, 4, 8, 16)
+constexpr int kMaxTrials = 4;
+__device__ __forceinline__ int greedy_trials(int k) { return k <= 2 ? 2 : (k == 4 ? 3 : 4); }
+
 struct Smem {
   float c[kMaxClusters];      // centroids in draw order
   float thr[kMaxClusters + 4];       // switch points between sorted neighbours, +inf padded
   uint32_t tcell[kMaxClusters + 4];  // cell of each switch point, kMaxCells beyond the last
   float sv[kMaxClusters];     // sorted distinct centroid values
   int sidx[kMaxClusters];     // lowest draw index holding each sorted value
-  double wred[8][2 * kMaxClusters];     // per-wave partial bins
+  union {
+    double wred[8][2 * kMaxClusters];   // per-wave partial bins (Lloyd rounds)
+    struct {                            // greedy k-means++ (seeding)
+      unsigned long long u[kMaxTrials - 1][kMaxClusters];  // draws of candidates 1..
+      unsigned long long pot[8][kMaxTrials];               // per-wave candidate potentials
+      float cand_c[kMaxTrials];
+      int cand_j[kMaxTrials];
+    } gk;
+  };
   float fred[2][8];                     // per-wave fp32 partials (double buffered)
   double dred[8];                       // per-wave fp64 partials
   unsigned long long ured[2][8];        // per-wave u64 partials (double buffered)
@@ -903,6 +915,16 @@ void any4_rows_kernel(const LaunchArgs args) {
       philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
       S.u[tid] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
     }
+    if (init == INIT_GREEDY && tid < k * (greedy_trials(k) - 1)) {
+      // greedy candidates s >= 1 of draw t: counter word t + 16 restart + 65536 s
+      const int s = 1 + tid / k, t = tid - (s - 1) * k;
+      const uint64_t rid = static_cast<uint64_t>(M.row_offset + row);
+      uint32_t c[4] = {static_cast<uint32_t>(rid),
+                       static_cast<uint32_t>(t + 16 * restart) + 65536u * static_cast<uint32_t>(s),
+                       static_cast<uint32_t>(M.matrix_index), static_cast<uint32_t>(rid >> 32)};
+      philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
+      S.gk.u[s - 1][t] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
+    }
     float pv[E];
     float lmax = 0.0f;  // this lane's largest sampling weight for the coming draw
 #pragma unroll
@@ -939,38 +961,80 @@ void any4_rows_kernel(const LaunchArgs args) {
           }
         }
         const unsigned long long excl = woff + incl - ls;
-        const unsigned long long r = __umul64hi(S.u[t], Q);
-        const bool own = ls > 0 && excl <= r && r - excl < ls;
-        // the owner's wave finds the element: the owner lane stages its weights and
-        // values, and lane m of that wave takes element m (one wave, so no block barrier)
-        if (__ballot(own) != 0ull) {
-          if (own) {
-            S.owner = tid;
-            S.owner_excl = excl;
+        // greedy k-means++ searches several candidates (s >= 1 land in S.gk); the plain
+        // draw is candidate 0
+        const int n_cand = (init == INIT_GREEDY && t > 0) ? greedy_trials(k) : 1;
+        for (int s = 0; s < n_cand; ++s) {
+          const unsigned long long r = __umul64hi(s == 0 ? S.u[t] : S.gk.u[s - 1][t], Q);
+          const bool own = ls > 0 && excl <= r && r - excl < ls;
+          // the owner's wave finds the element: the owner lane stages its weights and
+          // values, and lane m of that wave takes element m (one wave, so no block barrier)
+          if (__ballot(own) != 0ull) {
+            if (own) {
+              S.owner = tid;
+              S.owner_excl = excl;
 #pragma unroll
-            for (int v = 0; v < E / 4; ++v) {
-              reinterpret_cast<float4*>(S.stage_p)[v] =
-                  make_float4(pv[4 * v], pv[4 * v + 1], pv[4 * v + 2], pv[4 * v + 3]);
-              reinterpret_cast<float4*>(S.stage_x)[v] =
-                  make_float4(xv[4 * v], xv[4 * v + 1], xv[4 * v + 2], xv[4 * v + 3]);
+              for (int v = 0; v < E / 4; ++v) {
+                reinterpret_cast<float4*>(S.stage_p)[v] =
+                    make_float4(pv[4 * v], pv[4 * v + 1], pv[4 * v + 2], pv[4 * v + 3]);
+                reinterpret_cast<float4*>(S.stage_x)[v] =
+                    make_float4(xv[4 * v], xv[4 * v + 1], xv[4 * v + 2], xv[4 * v + 3]);
+              }
+            }
+            wave_lds_fence();
+            const unsigned long long oex = S.owner_excl;
+            const double q = (lane < E) ? floor(static_cast<double>(S.stage_p[lane]) * sc) : 0.0;
+            const double qi = wave_incl_scan_f64(q);
+            const bool hit = lane < E && oex + static_cast<unsigned long long>(qi) > r;
+            const unsigned long long bal = __ballot(hit);
+            int ms = __ffsll(static_cast<long long>(bal)) - 1;
+            if (ms < 0) ms = E - 1;  // unreachable: the owner's prefix always crosses r
+            if (lane == 0) {
+              if (s == 0) {
+                S.pick_c = S.stage_x[ms];
+                S.pick_j = S.owner * E + ms;
+              } else {
+                S.gk.cand_c[s] = S.stage_x[ms];
+                S.gk.cand_j[s] = S.owner * E + ms;
+              }
             }
           }
-          wave_lds_fence();
-          const unsigned long long oex = S.owner_excl;
-          const double q = (lane < E) ? floor(static_cast<double>(S.stage_p[lane]) * sc) : 0.0;
-          const double qi = wave_incl_scan_f64(q);
-          const bool hit = lane < E && oex + static_cast<unsigned long long>(qi) > r;
-          const unsigned long long bal = __ballot(hit);
-          int ms = __ffsll(static_cast<long long>(bal)) - 1;
-          if (ms < 0) ms = E - 1;  // unreachable: the owner's prefix always crosses r
-          if (lane == 0) {
-            S.pick_c = S.stage_x[ms];
-            S.pick_j = S.owner * E + ms;
-          }
+          __syncthreads();
         }
-        __syncthreads();
         ct = S.pick_c;
         pick = S.pick_j;
+        if (n_cand > 1) {
+          // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * sc): exact
+          // integers (per lane below 2^47 in fp64, per row in u64), compared exactly
+          for (int s = 0; s < n_cand; ++s) {
+            const float cs = s == 0 ? ct : S.gk.cand_c[s];
+            double lp = 0.0;
+#pragma unroll
+            for (int m = 0; m < E; ++m) {
+              float d = xv[m] - cs;
+              d = d * d;
+              const int pm = min(__float_as_int(pv[m]), __float_as_int(av[m] * d));
+              lp += floor(static_cast<double>(__int_as_float(pm)) * sc);
+            }
+            const unsigned long long tot =
+                readlane_u64(wave_incl_scan_u64(static_cast<unsigned long long>(lp)), kWave - 1);
+            if (lane == 0) S.gk.pot[wave][s] = tot;
+          }
+          __syncthreads();
+          unsigned long long best = 0;
+          for (int s = 0; s < n_cand; ++s) {
+            unsigned long long pot = 0;
+            for (int w = 0; w < nw; ++w) pot += S.gk.pot[w][s];
+            if (s == 0 || pot < best) {
+              best = pot;
+              if (s > 0) {
+                ct = S.gk.cand_c[s];
+                pick = S.gk.cand_j[s];
+              }
+            }
+          }
+          __syncthreads();  // S.gk.pot is read before the next draw writes it
+        }
       }
       if (tid == 0) {
         S.c[t] = ct;

@@ -44,7 +44,7 @@ constexpr int32_t kVarInitShift = 2;          // init: 0 k-means++, 1 random, 2 
 constexpr int32_t kVarSymmetric = 1 << 4;     // Eq. 3 scaling
 constexpr int32_t kVarRestartShift = 8;       // bits 8-15: restarts - 1
 constexpr int32_t kVarKnownBits = 0xFF1F;
-enum : int32_t { INIT_KMEANSPP = 0, INIT_RANDOM = 1, INIT_UNIFORM = 2 };
+enum : int32_t { INIT_KMEANSPP = 0, INIT_RANDOM = 1, INIT_UNIFORM = 2, INIT_GREEDY = 3 };
 
 struct LaunchArgs {
   MatDesc m[kMaxMats];
