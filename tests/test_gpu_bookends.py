@@ -291,6 +291,24 @@ def test_gemv_random_fields(case):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))      # fixed summation order
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("M", list(range(1, 9)))
+def test_gemv_every_token_count(M, dtype):
+    """Every instance (1, 2, 4, 8 token slots x bf16/fp32 x) on a ragged row count, and
+    the smallest K (one 16-column chunk per row)."""
+    rng = np.random.default_rng(300 + M + 10 * dtype)
+    for N, K, g in ((37, 1536, 32), (5, 16, 16)):
+        codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        lut = (rng.standard_normal((N, 16)) * 3).astype(np.float16).view(np.uint16)
+        scale = rng.lognormal(-4, 1, (N, K // g)).astype(np.float16).view(np.uint16)
+        offset = (rng.standard_normal((N, K // g)) * 0.1).astype(np.float16).view(np.uint16)
+        x = draw_activations(rng, M, draw_act(rng, K), dtype)
+        q = any4().Quantized(codes=_dev(codes), lut=torch.from_numpy(lut.view(np.float16)).cuda(),
+                             scale=torch.from_numpy(scale.view(np.float16)).cuda(),
+                             offset=torch.from_numpy(offset.view(np.float16)).cuda(), objective=None)
+        _check_gemv(q, g, 16, codes, lut, scale, offset, x, dtype, f"M{M}/N{N}/K{K}")
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_gemv_full_up_proj_sampled_rows(M):
     """The quantized 14336 x 4096 up_proj times M calibration-like tokens (the launch
