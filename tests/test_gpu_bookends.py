@@ -162,8 +162,15 @@ def test_dequant_empty_and_invalid():
                          offset=torch.empty((0, 1), dtype=torch.float16, device="cuda"),
                          objective=None)
     assert any4().dequantize(q, 128, 16).shape == (0, 128)
+    q96 = any4().Quantized(codes=torch.empty((0, 96), dtype=torch.uint8, device="cuda"),
+                           lut=torch.empty((0, 16), dtype=torch.float16, device="cuda"),
+                           scale=torch.empty((0, 2), dtype=torch.float16, device="cuda"),
+                           offset=torch.empty((0, 2), dtype=torch.float16, device="cuda"),
+                           objective=None)
     with pytest.raises(any4().Any4Error):
-        any4().dequantize(q, 96, 16)            # group not a power of two
+        any4().dequantize(q96, 96, 16)          # group not a power of two (the ABI's check)
+    with pytest.raises(ValueError):
+        any4().dequantize(q, 64, 16)            # scale/offset extents do not match the group
 
 
 # --- end to end ---------------------------------------------------------------------------
@@ -338,5 +345,16 @@ def test_gemv_unsupported_and_invalid():
                        torch.zeros((2, 4), device="cuda"))
     with pytest.raises(any4().Any4Error):
         any4().lut_gemv(q, torch.ones((9, 512), device="cuda"))        # more than 8 tokens
+    q8 = any4().Quantized(codes=q.codes, lut=q.lut,
+                          scale=torch.zeros((4, 64), dtype=torch.float16, device="cuda"),
+                          offset=torch.zeros((4, 64), dtype=torch.float16, device="cuda"),
+                          objective=None)
     with pytest.raises(any4().Any4Error):
-        any4().lut_gemv(q, torch.ones((1, 512), device="cuda"), group=8)  # group below 16
+        any4().lut_gemv(q8, torch.ones((1, 512), device="cuda"), group=8)  # group below 16
+    # extents the C ABI cannot see are checked by the binding
+    with pytest.raises(ValueError):
+        any4().lut_gemv(q, torch.ones((1, 512), device="cuda"), n_clusters=8)   # lut is [4, 16]
+    with pytest.raises(ValueError):
+        any4().lut_gemv(q, torch.ones((1, 256), device="cuda"))                 # x too short
+    with pytest.raises(ValueError):
+        any4().lut_gemv(q, torch.ones((1, 512), device="cuda"), out=torch.empty((1, 3), device="cuda"))

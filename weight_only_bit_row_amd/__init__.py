@@ -294,17 +294,41 @@ def act_absmean(x, out=None, ws=None):
     return out
 
 
+def _check_quantized(q: Quantized, group: int, n_clusters: int):
+    """The C ABI takes bare pointers, so the extents it will read are checked here: codes
+    [N, K/2] uint8, lut [N, n_clusters] fp16, scale and offset [N, K/group] fp16, all
+    contiguous on one GPU."""
+    torch = _torch()
+    _require_gpu(q.codes)
+    if q.codes.dim() != 2 or q.codes.dtype != torch.uint8:
+        raise ValueError("codes must be a [N, K/2] uint8 tensor")
+    N, K = int(q.codes.shape[0]), int(q.codes.shape[1]) * 2
+    if group < 1 or K % group != 0:
+        raise ValueError("group must divide K")
+    want = {"lut": ((N, n_clusters), q.lut), "scale": ((N, K // group), q.scale),
+            "offset": ((N, K // group), q.offset)}
+    for name, (shape, t) in want.items():
+        if tuple(t.shape) != shape or t.dtype != torch.float16:
+            raise ValueError(f"{name} must be a {list(shape)} float16 tensor, got "
+                             f"{list(t.shape)} {t.dtype}")
+    for t in (q.codes, q.lut, q.scale, q.offset):
+        if not t.is_contiguous() or t.device != q.codes.device:
+            raise ValueError("codes, lut, scale and offset must be contiguous on one device")
+    return N, K
+
+
 def dequantize(q: Quantized, group: int = 128, n_clusters: int = 16, out_dtype=None, out=None):
     """Eq. 4 dequantization alpha * LUT[q] + beta of a quantized matrix to [N, K]
     bf16 (default) or fp32."""
     torch = _torch()
-    _require_gpu(q.codes)
+    N, K = _check_quantized(q, group, n_clusters)
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
-    N, K = int(q.codes.shape[0]), int(q.codes.shape[1]) * 2
     if out is None:
         out = torch.empty((N, K), dtype=out_dtype, device=q.codes.device)
+    elif tuple(out.shape) != (N, K) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [N, K] tensor of out_dtype")
     m = Any4Matrix()
     m.n_rows, m.n_cols = N, K
     m.w_dtype = ANY4_F32
@@ -320,16 +344,17 @@ def lut_gemv(q: Quantized, x, group: int = 128, n_clusters: int = 16, out=None):
     """y [M, N] fp32 = x [M, K] (bf16/fp32, M <= 8) times the dequantized weight,
     transposed, without materializing it."""
     torch = _torch()
-    _require_gpu(q.codes)
+    N, K = _check_quantized(q, group, n_clusters)
     code, x = _dtype_code(x)
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous [M, K] tensor")
-    N, K = int(q.codes.shape[0]), int(q.codes.shape[1]) * 2
+    if x.dim() != 2 or not x.is_contiguous() or x.device != q.codes.device:
+        raise ValueError("x must be a contiguous [M, K] tensor on the codes' device")
     M = int(x.shape[0])
     if int(x.shape[1]) != K:
         raise ValueError("x has the wrong number of columns")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=q.codes.device)
+    elif tuple(out.shape) != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] float32 tensor")
     m = Any4Matrix()
     m.n_rows, m.n_cols = N, K
     m.w_dtype = ANY4_F32
