@@ -190,12 +190,29 @@ def _alloc_outputs(n, k_cols, group, n_clusters, device, with_objective):
     )
 
 
-def _matrix(w, act, out: Optional[Quantized], row_offset=0, matrix_index=0) -> Any4Matrix:
+def _matrix(w, act, out: Optional[Quantized], row_offset=0, matrix_index=0,
+            group: Optional[int] = None, n_clusters: Optional[int] = None) -> Any4Matrix:
+    torch = _torch()
     code, w = _dtype_code(w)
     if w.dim() != 2 or not w.is_contiguous():
         raise ValueError("W must be a contiguous [N, K] tensor")
-    if act.dim() != 1 or not act.is_contiguous() or act.dtype != _torch().float32:
-        raise ValueError("act_absmean must be a contiguous float32 [K] tensor")
+    if (act.dim() != 1 or not act.is_contiguous() or act.dtype != torch.float32
+            or act.numel() != w.shape[1] or act.device != w.device):
+        raise ValueError("act_absmean must be a contiguous float32 [K] tensor on W's device")
+    if out is not None and group is not None and n_clusters is not None:
+        # caller-provided outputs: the kernels write exactly these extents
+        N, K = int(w.shape[0]), int(w.shape[1])
+        if group < 1 or K % group != 0 or K % 2 != 0:
+            raise ValueError("group must divide K, and K must be even")
+        want = [("codes", out.codes, (N, K // 2), torch.uint8),
+                ("lut", out.lut, (N, n_clusters), torch.float16),
+                ("scale", out.scale, (N, K // group), torch.float16),
+                ("offset", out.offset, (N, K // group), torch.float16)]
+        if out.objective is not None:
+            want.append(("objective", out.objective, (N,), torch.float64))
+        for name, t, shape, dt in want:
+            if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device != w.device:
+                raise ValueError(f"out.{name} must be a contiguous {list(shape)} {dt} tensor on W's device")
     m = Any4Matrix()
     m.w = _ptr(w)
     m.w_dtype = code
@@ -235,7 +252,8 @@ def quantize_batch(items: Sequence[Tuple[object, object]], group: int = 128, n_c
     for i, (w, act) in enumerate(items):
         mats[i] = _matrix(w, act, outputs[i],
                           row_offset=(row_offsets[i] if row_offsets else 0),
-                          matrix_index=(matrix_indices[i] if matrix_indices else i))
+                          matrix_index=(matrix_indices[i] if matrix_indices else i),
+                          group=group, n_clusters=n_clusters)
     need = workspace_bytes(mats, len(items), p)
     if ws is None or ws.numel() < need:
         ws = workspace(device, need)
@@ -253,7 +271,7 @@ def quantize(w, act, group: int = 128, n_clusters: int = 16, iters: int = 20, se
     p = params(group, n_clusters, iters, seed, variant)
     if out is None:
         out = _alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, w.device, with_objective)
-    m = _matrix(w, act, out, row_offset, matrix_index)
+    m = _matrix(w, act, out, row_offset, matrix_index, group, n_clusters)
     need = WORKSPACE_BYTES if variant >> 8 == 0 else workspace_bytes(ctypes.byref(m), 1, p)
     if ws is None or ws.numel() < need:
         ws = workspace(w.device, need)
@@ -286,6 +304,8 @@ def act_absmean(x, out=None, ws=None):
     T, K = int(x.shape[0]), int(x.shape[1])
     if out is None:
         out = torch.empty((K,), dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != (K,) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [K] tensor")
     need = act_absmean_workspace_bytes(T, K)
     if ws is None or ws.numel() < need:
         ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
