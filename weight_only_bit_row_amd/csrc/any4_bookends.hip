@@ -306,7 +306,8 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
 // the only large operand (half a byte per weight), x is a few KB that every wave reads
 // through L1/L2.
 //
-// One wave owns R = 4 rows and one K-slice.  Lane l takes the 16-column chunks
+// One wave owns R rows (4, or 2 for eight tokens on rows up to 16384 columns) and one
+// K-slice.  Lane l takes the 16-column chunks
 // l, l + 64, ... of the slice for all R rows, so each 8-byte code load is part of a
 // 512-byte contiguous run per row and each x value, converted once, serves R rows.
 // The row LUTs sit in LDS, 16 floats per row; a nibble's LDS address is formed by one
@@ -374,19 +375,20 @@ __device__ __forceinline__ void gv_load_x_raw(const GemvDesc& d, uint32_t col, G
   }
 }
 
-// Rows per wave.  Four measured best at one and two tokens on 4096 x 14336 and
-// 14336 x 4096 (eight halves the wave count and hides less latency, two converts x for
-// fewer rows), and keeps the eight-token instance within the register file.
-template <int MT>
-constexpr int gv_rows() { return 4; }
+// Rows per wave (R).  Four measured best for one to four tokens on 14336 x 4096,
+// 4096 x 14336 and 8192 x 28672 (eight halves the wave count and hides less latency,
+// two converts x for fewer rows).  With eight tokens the four-row instance needs ~230
+// VGPRs (two waves per SIMD) and short rows leave its x loads exposed: two rows per wave
+// measured 30% faster up to K = 16384, four rows 9% faster at K = 28672.
+constexpr int kGvLongK = 16384;
 
-template <int MT, bool XBF>
+template <int MT, bool XBF, int R>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int split_log2) {
-  constexpr int R = gv_rows<MT>();
   constexpr int XW = MT <= 2 ? 8 : 4;   // x columns converted per step (register budget)
   constexpr bool PX = MT <= 2;          // x of the next chunk prefetched with its codes (else
                                         // this chunk's x is loaded with the next codes)
-  __shared__ __attribute__((aligned(1024))) float lut[kGvWaves][R][16];
+  constexpr int RB = R < 4 ? 4 : R;     // LUT rows per wave block (at least 256 bytes)
+  __shared__ __attribute__((aligned(1024))) float lut[kGvWaves][RB][16];
   __shared__ float part[kGvWaves][R * MT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -398,12 +400,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
   const int gshift = __builtin_ctz(static_cast<uint32_t>(d.group));
   const int64_t G = K >> gshift;
   // the wave's LUT entries (16 per row) are fetched first and stored below
-  static_assert(R % 4 == 0, "R rows of 16 LUT entries are loaded 64 at a time");
-  uint16_t lut_bits[R / 4];
+  static_assert(RB % 4 == 0, "LUT rows of 16 entries are loaded 64 at a time");
+  uint16_t lut_bits[RB / 4];
 #pragma unroll
-  for (int i = 0; i < R / 4; ++i) {
+  for (int i = 0; i < RB / 4; ++i) {
     const int r = (lane >> 4) + 4 * i, q = lane & 15;
-    const bool ok = row0 + r < N && q < d.n_clusters;
+    const bool ok = r < R && row0 + r < N && q < d.n_clusters;
     lut_bits[i] = d.lut[ok ? (row0 + r) * d.n_clusters + q : 0];  // no branch
   }
   const uint8_t* codes[R];
@@ -436,17 +438,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
   load_w(wcur, c < c_last ? c : c_last);
   if constexpr (PX) gv_load_x_raw<MT, XBF>(d, (c < c_last ? c : c_last) << 4, xcur);
 #pragma unroll
-  for (int i = 0; i < R / 4; ++i) {
+  for (int i = 0; i < RB / 4; ++i) {
     const int r = (lane >> 4) + 4 * i, q = lane & 15;
-    lut[wave][r][q] = (row0 + r < N && q < d.n_clusters) ? half_bits_to_float(lut_bits[i])
-                                                          : __builtin_nanf("");
+    lut[wave][r][q] = (r < R && row0 + r < N && q < d.n_clusters) ? half_bits_to_float(lut_bits[i])
+                                                                   : __builtin_nanf("");
   }
   // each wave reads only its own LUT block; LDS operations of a wave complete in order
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // byte 0 of a LUT address comes from the codes, bytes 1..3 from the wave's block
-  const uint32_t block = static_cast<uint32_t>(wave) * (R * 64u);
+  const uint32_t block = static_cast<uint32_t>(wave) * (RB * 64u);
   const char* lut_bytes = reinterpret_cast<const char*>(&lut[0][0][0]);
   float y[R][MT];
 #pragma unroll
@@ -612,26 +614,26 @@ int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave) {
   return l;
 }
 
-template <int MT>
+template <int MT, int R>
 hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
-  constexpr int R = gv_rows<MT>();
   const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R);
   const int64_t groups = (d.n_rows + R - 1) / R;
   const int64_t per_wg = kGvWaves >> l;
   const dim3 grid(static_cast<uint32_t>((groups + per_wg - 1) / per_wg));
   if (d.x_bf16)
-    hipLaunchKernelGGL((gemv_kernel<MT, true>), grid, dim3(kThreads), 0, stream, d, l);
+    hipLaunchKernelGGL((gemv_kernel<MT, true, R>), grid, dim3(kThreads), 0, stream, d, l);
   else
-    hipLaunchKernelGGL((gemv_kernel<MT, false>), grid, dim3(kThreads), 0, stream, d, l);
+    hipLaunchKernelGGL((gemv_kernel<MT, false, R>), grid, dim3(kThreads), 0, stream, d, l);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
-  if (d.n_tokens <= 1) return launch_gemv_mt<1>(d, stream);
-  if (d.n_tokens <= 2) return launch_gemv_mt<2>(d, stream);
-  if (d.n_tokens <= 4) return launch_gemv_mt<4>(d, stream);
-  return launch_gemv_mt<8>(d, stream);
+  if (d.n_tokens <= 1) return launch_gemv_mt<1, 4>(d, stream);
+  if (d.n_tokens <= 2) return launch_gemv_mt<2, 4>(d, stream);
+  if (d.n_tokens <= 4) return launch_gemv_mt<4, 4>(d, stream);
+  if (d.n_cols <= kGvLongK) return launch_gemv_mt<8, 2>(d, stream);
+  return launch_gemv_mt<8, 4>(d, stream);
 }
 
 hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream) {
