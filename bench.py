@@ -140,12 +140,30 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     def run_gv8():
         any4.lut_gemv(q, x8, g, k, out=y8)
 
+    # a Llama-70B down_proj-sized product (8192 x 28672): seeded random codes, LUTs and
+    # group scales (the kernel's time does not depend on the values)
+    N70, K70 = 8192, 28672
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(70)
+    q70 = any4.Quantized(
+        codes=torch.randint(0, 256, (N70, K70 // 2), dtype=torch.uint8, device=dev, generator=gen),
+        lut=torch.randn((N70, k), device=dev, generator=gen).half(),
+        scale=(torch.rand((N70, K70 // g), device=dev, generator=gen) * 1e-2).half(),
+        offset=(torch.randn((N70, K70 // g), device=dev, generator=gen) * 1e-2).half(),
+        objective=None)
+    x70 = torch.randn((1, K70), device=dev, generator=gen).bfloat16()
+    y70 = torch.empty((1, N70), dtype=torch.float32, device=dev)
+
+    def run_gv70():
+        any4.lut_gemv(q70, x70, g, k, out=y70)
+
     if profile_steps:
         for _ in range(profile_steps):
             run_abs()
             run_dq()
             run_gv1()
             run_gv8()
+            run_gv70()
         torch.cuda.synchronize()
         return None
 
@@ -165,6 +183,10 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     ms_dq = per_launch_ms(run_dq, 100)
     ms_gv1 = per_launch_ms(run_gv1, 200)
     ms_gv8 = per_launch_ms(run_gv8, 100)
+    ms_gv70 = per_launch_ms(run_gv70, 100)
+    w70 = any4.dequantize(q70, g, k)
+    ms_mm70 = per_launch_ms(lambda: torch.nn.functional.linear(x70, w70), 50)
+    del w70
     run_dq()
     ms_mm1 = per_launch_ms(lambda: torch.nn.functional.linear(x1, w_hat), 200)
     ms_mm8 = per_launch_ms(lambda: torch.nn.functional.linear(x8, w_hat), 100)
@@ -172,8 +194,9 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     bytes_w = N * K // 2 + N * k * 2 + 2 * N * (K // g) * 2     # codes, LUT, alpha/beta
     bytes_dq = bytes_w + N * K * 2                                # + bf16 out
 
-    def bytes_gv(M):
-        return bytes_w + M * K * 2 + M * N * 4                    # + bf16 x, fp32 y
+    def bytes_gv(M, n=N, kk=K):
+        wb = n * kk // 2 + n * k * 2 + 2 * n * (kk // g) * 2
+        return wb + M * kk * 2 + M * n * 4                        # + bf16 x, fp32 y
 
     def roof(nbytes, ms, key):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -199,6 +222,11 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
          "workload": f"eight calibration tokens times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv8, "bf16_matmul_ms_per_call": ms_mm8,
          "roofline": roof(bytes_gv(8), ms_gv8, "gemv8_traffic_bytes_per_launch")},
+        {"kernel": "any4_lut_gemv (gemv_kernel<1, bf16 x, 4 rows per wave>)",
+         "workload": f"one token times a {N70}x{K70} matrix of seeded random codes (Llama-70B "
+                     f"down_proj size), fp32 out",
+         "ms_per_call": ms_gv70, "bf16_matmul_ms_per_call": ms_mm70,
+         "roofline": roof(bytes_gv(1, N70, K70), ms_gv70, "gemv70_traffic_bytes_per_launch")},
     ]
 
 
