@@ -229,9 +229,9 @@ int any4_dequantize(const any4_matrix* m, const any4_params* params, void* w_out
  * exact evaluation of the Eq. 4 definition the error stays within 1e-5 of
  * sum_j |x_j| (|alpha*LUT[q_j]| + |beta|), and the summation order is fixed (repeated calls
  * give identical bits).  Supports 1 <= n_tokens <= 8, n_cols and group multiples of 16,
- * codes 8-byte and x 16-byte aligned (ANY4_ERR_UNSUPPORTED otherwise; use
- * any4_dequantize and a GEMM for larger batches).  A code at or above n_clusters gives
- * NaN.  Errors:
+ * n_rows and n_cols below 2^31, codes 8-byte and x 16-byte aligned (ANY4_ERR_UNSUPPORTED
+ * otherwise; use any4_dequantize and a GEMM for larger batches).  A code at or above
+ * n_clusters gives NaN.  Errors:
  * ANY4_ERR_INVALID_ARG (NULL pointer, bad sizes or dtype), ANY4_ERR_UNSUPPORTED,
  * ANY4_ERR_HIP. */
 int any4_lut_gemv(const any4_matrix* m, const any4_params* params, const void* x, int32_t x_dtype,

@@ -177,6 +177,7 @@ def test_lut_gemv_validates_before_launch(L):
     odd.codes = 0x3004
     assert gemv(ctypes.byref(odd), ctypes.byref(p), 0x7000, 1, 1, y, None) == 2
     assert gemv(ctypes.byref(m), ctypes.byref(p), 0x7008, 1, 1, y, None) == 2   # x alignment
+    assert gemv(ctypes.byref(_mat(k=1 << 31)), ctypes.byref(p), 0x7000, 1, 1, y, None) == 2
     m0 = any4.Any4Matrix()
     m0.n_rows, m0.n_cols = 0, 256
     assert gemv(ctypes.byref(m0), ctypes.byref(p), None, 1, 1, None, None) == 0

@@ -442,7 +442,8 @@ int any4_lut_gemv(const any4_matrix* m, const any4_params* params, const void* x
   if (n_tokens < 1) return ANY4_ERR_INVALID_ARG;
   if (n_tokens > any4::kGemvMaxTokens || m->n_cols % 16 != 0 || params->group % 16 != 0)
     return ANY4_ERR_UNSUPPORTED;
-  if (m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  // rows index the grid and column offsets within a row are 32-bit in the kernel
+  if (m->n_rows > INT32_MAX || m->n_cols > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
   if (m->n_rows == 0) return ANY4_OK;
   if (!m->codes || !m->lut || !m->scale || !m->offset || !x || !y) return ANY4_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(m->codes) & 7) != 0 || (reinterpret_cast<uintptr_t>(x) & 15) != 0)
