@@ -214,7 +214,7 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
          "workload": f"Eq. 4 dequantization of the quantized {N}x{K} up_proj (group {g}, "
                      f"{k} clusters) to bf16",
          "ms_per_call": ms_dq, "roofline": roof(bytes_dq, ms_dq, "dequant_traffic_bytes_per_launch")},
-        {"kernel": "any4_lut_gemv (gemv_kernel<1, bf16 x, 4 rows per wave>)",
+        {"kernel": "any4_lut_gemv (gemv_kernel<1, bf16 x, 2 rows per wave>)",
          "workload": f"one calibration token times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv1, "bf16_matmul_ms_per_call": ms_mm1,
          "roofline": roof(bytes_gv(1), ms_gv1, "gemv1_traffic_bytes_per_launch")},

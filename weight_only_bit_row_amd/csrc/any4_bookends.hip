@@ -306,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
 // the only large operand (half a byte per weight), x is a few KB that every wave reads
 // through L1/L2.
 //
-// One wave owns R rows (4, or 2 for eight tokens on rows up to 16384 columns) and one
-// K-slice.  Lane l takes the 16-column chunks
+// One wave owns R rows (2 on rows up to 16384 columns except at four tokens, else 4) and
+// one K-slice.  Lane l takes the 16-column chunks
 // l, l + 64, ... of the slice for all R rows, so each 8-byte code load is part of a
 // 512-byte contiguous run per row and each x value, converted once, serves R rows.
 // The row LUTs sit in LDS, 16 floats per row; a nibble's LDS address is formed by one
@@ -375,11 +375,12 @@ __device__ __forceinline__ void gv_load_x_raw(const GemvDesc& d, uint32_t col, G
   }
 }
 
-// Rows per wave (R).  Four measured best for one to four tokens on 14336 x 4096,
-// 4096 x 14336 and 8192 x 28672 (eight halves the wave count and hides less latency,
-// two converts x for fewer rows).  With eight tokens the four-row instance needs ~230
-// VGPRs (two waves per SIMD) and short rows leave its x loads exposed: two rows per wave
-// measured 30% faster up to K = 16384, four rows 9% faster at K = 28672.
+// Rows per wave (R), chosen by row length.  Up to K = 16384 ("short rows") a wave takes 2
+// rows: more waves hide more of the LUT-read and load latency (one token: 5% faster on
+// 14336 x 4096; eight tokens: 30% faster, where the four-row instance needs ~230 VGPRs).
+// Longer rows take 4, which converts each x value for more rows (one token, 8192 x 28672:
+// 9% faster than two rows).  Four tokens keep 4 rows at every length (measured best).
+// Eight rows per wave halve the wave count and were slower everywhere.
 constexpr int kGvLongK = 16384;
 
 template <int MT, bool XBF, int R>
@@ -605,18 +606,20 @@ hipError_t launch_absmean(const void* x, int dtype, int64_t n_tokens, int64_t n_
   return hipGetLastError();
 }
 
-int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave) {
-  // split K over up to 4 waves of a workgroup while the grid holds fewer than 2048
-  // waves (8 per CU) and every lane keeps at least two chunks of its slice
+int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave, int64_t target) {
+  // split K over up to 4 waves of a workgroup while the grid holds fewer than `target`
+  // waves and every lane keeps at least two chunks of its slice
   const int64_t groups = (n_rows + rows_per_wave - 1) / rows_per_wave, chunks = n_cols / 16;
   int l = 0;
-  while ((1 << l) < kGvWaves && groups << l < 2048 && chunks >> (l + 1) >= 128) ++l;
+  while ((1 << l) < kGvWaves && groups << l < target && chunks >> (l + 1) >= 128) ++l;
   return l;
 }
 
 template <int MT, int R>
 hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
-  const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R);
+  // one or two tokens: short waves whose LUT reads want latency hiding, 16 waves per CU;
+  // more tokens: 8 per CU (more registers per wave)
+  const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R, MT <= 2 ? 4096 : 2048);
   const int64_t groups = (d.n_rows + R - 1) / R;
   const int64_t per_wg = kGvWaves >> l;
   const dim3 grid(static_cast<uint32_t>((groups + per_wg - 1) / per_wg));
@@ -629,11 +632,13 @@ hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
 
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
-  if (d.n_tokens <= 1) return launch_gemv_mt<1, 4>(d, stream);
-  if (d.n_tokens <= 2) return launch_gemv_mt<2, 4>(d, stream);
+  const bool short_rows = d.n_cols <= kGvLongK;
+  if (d.n_tokens <= 1)
+    return short_rows ? launch_gemv_mt<1, 2>(d, stream) : launch_gemv_mt<1, 4>(d, stream);
+  if (d.n_tokens <= 2)
+    return short_rows ? launch_gemv_mt<2, 2>(d, stream) : launch_gemv_mt<2, 4>(d, stream);
   if (d.n_tokens <= 4) return launch_gemv_mt<4, 4>(d, stream);
-  if (d.n_cols <= kGvLongK) return launch_gemv_mt<8, 2>(d, stream);
-  return launch_gemv_mt<8, 4>(d, stream);
+  return short_rows ? launch_gemv_mt<8, 2>(d, stream) : launch_gemv_mt<8, 4>(d, stream);
 }
 
 hipError_t launch_dequant(const DequantDesc& d, hipStream_t stream) {
