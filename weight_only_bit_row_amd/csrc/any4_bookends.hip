@@ -306,8 +306,7 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
 // the only large operand (half a byte per weight), x is a few KB that every wave reads
 // through L1/L2.
 //
-// One wave owns R rows (2 on rows up to 16384 columns except at four tokens, else 4) and
-// one K-slice.  Lane l takes the 16-column chunks
+// One wave owns R rows (2 on rows up to 16384 columns, else 4) and one K-slice.  Lane l takes the 16-column chunks
 // l, l + 64, ... of the slice for all R rows, so each 8-byte code load is part of a
 // 512-byte contiguous run per row and each x value, converted once, serves R rows.
 // The row LUTs sit in LDS, 16 floats per row; a nibble's LDS address is formed by one
@@ -379,8 +378,8 @@ __device__ __forceinline__ void gv_load_x_raw(const GemvDesc& d, uint32_t col, G
 // rows: more waves hide more of the LUT-read and load latency (one token: 5% faster on
 // 14336 x 4096; eight tokens: 30% faster, where the four-row instance needs ~230 VGPRs).
 // Longer rows take 4, which converts each x value for more rows (one token, 8192 x 28672:
-// 9% faster than two rows).  Four tokens keep 4 rows at every length (measured best).
-// Eight rows per wave halve the wave count and were slower everywhere.
+// 9% faster than two rows).  Eight rows per wave halve the wave count and were slower
+// everywhere.
 constexpr int kGvLongK = 16384;
 
 template <int MT, bool XBF, int R>
@@ -617,9 +616,9 @@ int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave, int6
 
 template <int MT, int R>
 hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
-  // one or two tokens: short waves whose LUT reads want latency hiding, 16 waves per CU;
-  // more tokens: 8 per CU (more registers per wave)
-  const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R, MT <= 2 ? 4096 : 2048);
+  // up to four tokens: short waves whose LUT reads want latency hiding, 16 waves per CU;
+  // eight tokens: 8 per CU (more registers per wave)
+  const int l = plan_gemv_split_log2(d.n_rows, d.n_cols, R, MT <= 4 ? 4096 : 2048);
   const int64_t groups = (d.n_rows + R - 1) / R;
   const int64_t per_wg = kGvWaves >> l;
   const dim3 grid(static_cast<uint32_t>((groups + per_wg - 1) / per_wg));
@@ -637,7 +636,8 @@ hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
     return short_rows ? launch_gemv_mt<1, 2>(d, stream) : launch_gemv_mt<1, 4>(d, stream);
   if (d.n_tokens <= 2)
     return short_rows ? launch_gemv_mt<2, 2>(d, stream) : launch_gemv_mt<2, 4>(d, stream);
-  if (d.n_tokens <= 4) return launch_gemv_mt<4, 4>(d, stream);
+  if (d.n_tokens <= 4)
+    return short_rows ? launch_gemv_mt<4, 2>(d, stream) : launch_gemv_mt<4, 4>(d, stream);
   return short_rows ? launch_gemv_mt<8, 2>(d, stream) : launch_gemv_mt<8, 4>(d, stream);
 }
 
