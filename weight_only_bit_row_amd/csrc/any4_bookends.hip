@@ -302,20 +302,20 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
 // emitted format (the paper's tinygemm dequantizes on the fly before its multiply):
 //   y[m][n] = sum_j x[m][j] * (alpha_{n,g(j)} * LUT_n[q_{n,j}] + beta_{n,g(j)}),
 // taken per 16-column chunk c of one group as alpha * (sum_{j in c} x_j L_{q_j}) +
-// beta * (sum_{j in c} x_j), all in fp32.  HBM-bound at decode sizes: the codes are
-// the only large operand (half a byte per weight), x is a few KB that every wave reads
-// through L1/L2.
+// beta * (sum_{j in c} x_j), all in fp32.  Its roofline is HBM at decode sizes: the codes
+// are the only large operand (half a byte per weight); x is a few KB that every wave
+// reads through L1/L2.
 //
-// One wave owns R rows (2 on rows up to 16384 columns, else 4) and one K-slice.  Lane l takes the 16-column chunks
-// l, l + 64, ... of the slice for all R rows, so each 8-byte code load is part of a
-// 512-byte contiguous run per row and each x value, converted once, serves R rows.
-// The row LUTs sit in LDS, 16 floats per row; a nibble's LDS address is formed by one
-// byte permute that drops 4*q (shifted and masked, four nibbles per register) into
-// byte 0 of the wave's 256-byte LUT block (the row offset is an immediate).  All lanes
-// of a wave look up the same row at a time: 16 consecutive words, no bank conflicts.  Partial sums of the R*MT
-// outputs are reduced across the wave by a butterfly that halves the values held per
-// lane at each step, and across the K-slices of a row group through LDS, in a fixed
-// order (the result does not depend on timing).
+// One wave owns R rows (2 on rows up to 16384 columns, else 4) and one K-slice.  Lane l
+// takes the 16-column chunks l, l + 64, ... of the slice for all R rows, so each 8-byte
+// code load is part of a 512-byte contiguous run per row and each x value, converted
+// once, serves R rows.  The row LUTs sit in LDS, 16 floats per row; a nibble's LDS
+// address is formed by one byte permute that drops 4*q (shifted and masked, four nibbles
+// per register) into byte 0 of the wave's 256-byte LUT block (the row offset is an
+// immediate).  All lanes of a wave look up the same row at a time: 16 consecutive words,
+// no bank conflicts.  Partial sums of the R*MT outputs are reduced across the wave by a
+// butterfly that halves the values held per lane at each step, and across the K-slices
+// of a row group through LDS, in a fixed order (the result does not depend on timing).
 constexpr int kGvWaves = 4;    // waves per workgroup
 
 template <int N>
