@@ -943,10 +943,13 @@ void any4_rows_kernel(const LaunchArgs args) {
       } else {
         int e2;
         frexpf(pmax, &e2);
-        const double sc = ldexp(1.0, 40 - (e2 - 1));  // 2^(40 - floor(log2 pmax))
-        double lsum = floor(static_cast<double>(pv[0]) * sc);
+        // each term floor(p * 2^ksc), ksc = 40 - floor(log2 pmax), taken in fp32: the
+        // power-of-two scale is exact (p * 2^ksc < 2^41; a result that underflows is below
+        // 1 and floors to 0 either way) and so is the floor, then widened to fp64 exactly
+        const int ksc = 40 - (e2 - 1);
+        double lsum = static_cast<double>(floorf(ldexpf(pv[0], ksc)));
 #pragma unroll
-        for (int m = 1; m < E; ++m) lsum += floor(static_cast<double>(pv[m]) * sc);
+        for (int m = 1; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
         const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
@@ -983,7 +986,7 @@ void any4_rows_kernel(const LaunchArgs args) {
             }
             wave_lds_fence();
             const unsigned long long oex = S.owner_excl;
-            const double q = (lane < E) ? floor(static_cast<double>(S.stage_p[lane]) * sc) : 0.0;
+            const double q = (lane < E) ? static_cast<double>(floorf(ldexpf(S.stage_p[lane], ksc))) : 0.0;
             const double qi = wave_incl_scan_f64(q);
             const bool hit = lane < E && oex + static_cast<unsigned long long>(qi) > r;
             const unsigned long long bal = __ballot(hit);
@@ -1004,7 +1007,7 @@ void any4_rows_kernel(const LaunchArgs args) {
         ct = S.pick_c;
         pick = S.pick_j;
         if (n_cand > 1) {
-          // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * sc): exact
+          // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * 2^ksc): exact
           // integers (per lane below 2^47 in fp64, per row in u64), compared exactly
           for (int s = 0; s < n_cand; ++s) {
             const float cs = s == 0 ? ct : S.gk.cand_c[s];
@@ -1014,7 +1017,7 @@ void any4_rows_kernel(const LaunchArgs args) {
               float d = xv[m] - cs;
               d = d * d;
               const int pm = min(__float_as_int(pv[m]), __float_as_int(av[m] * d));
-              lp += floor(static_cast<double>(__int_as_float(pm)) * sc);
+              lp += static_cast<double>(floorf(ldexpf(__int_as_float(pm), ksc)));
             }
             const unsigned long long tot =
                 readlane_u64(wave_incl_scan_u64(static_cast<unsigned long long>(lp)), kWave - 1);
