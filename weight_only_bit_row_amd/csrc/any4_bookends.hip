@@ -313,9 +313,13 @@ __global__ __launch_bounds__(kThreads) void dequant_scalar_kernel(const DequantD
 // address is formed by one byte permute that drops 4*q (shifted and masked, four nibbles
 // per register) into byte 0 of the wave's 256-byte LUT block (the row offset is an
 // immediate).  All lanes of a wave look up the same row at a time: 16 consecutive words,
-// no bank conflicts.  Partial sums of the R*MT outputs are reduced across the wave by a
-// butterfly that halves the values held per lane at each step, and across the K-slices
-// of a row group through LDS, in a fixed order (the result does not depend on timing).
+// no bank conflicts.  With two or more tokens each row's LUT is first expanded into a
+// 256-entry table indexed by a whole code byte (both of its elements' values, 8 bytes):
+// half the LDS reads and no nibble unpacking, at the cost of bank conflicts, which
+// measured 2-7% faster there and up to 6% slower at one token.  Partial sums of the R*MT
+// outputs are reduced across the wave by a butterfly that halves the values held per
+// lane at each step, and across the K-slices of a row group through LDS, in a fixed
+// order (the result does not depend on timing).
 constexpr int kGvWaves = 4;    // waves per workgroup
 
 template <int N>
@@ -389,6 +393,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
                                         // this chunk's x is loaded with the next codes)
   constexpr int RB = R < 4 ? 4 : R;     // LUT rows per wave block (at least 256 bytes)
   __shared__ __attribute__((aligned(1024))) float lut[kGvWaves][RB][16];
+  // two or more tokens: a per-row table indexed by a whole code byte holding both of its
+  // elements' LUT values, one 8-byte LDS read per two weights
+  constexpr bool PT = MT >= 2;
+  __shared__ __attribute__((aligned(16))) float2 ptab[PT ? kGvWaves : 1][PT ? R : 1][PT ? 256 : 1];
   __shared__ float part[kGvWaves][R * MT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -447,6 +455,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (PT) {
+    // entry b of row r: (LUT[b & 15], LUT[b >> 4]), the low nibble being the even column
+    for (int i = lane; i < 256 * R; i += 64) {
+      const int r = i >> 8, b = i & 255;
+      ptab[wave][r][b] = make_float2(lut[wave][r][b & 15], lut[wave][r][b >> 4]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   // byte 0 of a LUT address comes from the codes, bytes 1..3 from the wave's block
   const uint32_t block = static_cast<uint32_t>(wave) * (RB * 64u);
   const char* lut_bytes = reinterpret_cast<const char*>(&lut[0][0][0]);
@@ -475,12 +493,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // the two 8-nibble words of the chunk
-      uint32_t lo4[R], hi4[R];
+      uint32_t wr[R], lo4[R], hi4[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const uint32_t w = h ? wcur.cw[r].y : wcur.cw[r].x;
-        lo4[r] = (w << 2) & 0x3C3C3C3Cu;   // 4 * nibbles 0, 2, 4, 6
-        hi4[r] = (w >> 2) & 0x3C3C3C3Cu;   // 4 * nibbles 1, 3, 5, 7
+        wr[r] = h ? wcur.cw[r].y : wcur.cw[r].x;
+        if constexpr (!PT) {
+          lo4[r] = (wr[r] << 2) & 0x3C3C3C3Cu;   // 4 * nibbles 0, 2, 4, 6
+          hi4[r] = (wr[r] >> 2) & 0x3C3C3C3Cu;   // 4 * nibbles 1, 3, 5, 7
+        }
       }
 #pragma unroll
       for (int qq = 0; qq < 8 / XW; ++qq) {  // XW columns of x at a time
@@ -512,11 +532,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
         for (int r = 0; r < R; ++r) {
 #pragma unroll
           for (int jj = 0; jj < XW / 2; ++jj) {
-            const uint32_t sel = 0x07060500u | uint32_t(jj + (XW / 2) * qq);
-            const float le = *reinterpret_cast<const float*>(
-                lut_bytes + __builtin_amdgcn_perm(block, lo4[r], sel) + r * 64);
-            const float lo = *reinterpret_cast<const float*>(
-                lut_bytes + __builtin_amdgcn_perm(block, hi4[r], sel) + r * 64);
+            const int jb = jj + (XW / 2) * qq;  // code byte within the word
+            float le, lo;
+            if constexpr (PT) {
+              const float2 L = ptab[wave][r][(wr[r] >> (8 * jb)) & 0xFFu];
+              le = L.x;
+              lo = L.y;
+            } else {
+              const uint32_t sel = 0x07060500u | uint32_t(jb);
+              le = *reinterpret_cast<const float*>(
+                  lut_bytes + __builtin_amdgcn_perm(block, lo4[r], sel) + r * 64);
+              lo = *reinterpret_cast<const float*>(
+                  lut_bytes + __builtin_amdgcn_perm(block, hi4[r], sel) + r * 64);
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               acc[r][m] = fmaf(xv[m][2 * jj], le, acc[r][m]);
