@@ -185,8 +185,8 @@ def test_lut_gemv_validates_before_launch(L):
 def test_launch_geometry(L):
     assert any4.launch_geometry(4096) == (32, 2)
     assert any4.launch_geometry(512) == (8, 1)
-    e, nw = any4.launch_geometry(28672)
-    assert e * nw * 64 >= 28672 and nw <= 8
+    assert any4.launch_geometry(28672) == (32, 14)
+    assert any4.launch_geometry(32768) == (32, 16)
     for k in [2, 100, 1000, 2048, 14336, 32768]:
         e, nw = any4.launch_geometry(k)
         assert e * nw * 64 >= k

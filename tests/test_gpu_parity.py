@@ -30,11 +30,11 @@ def any4():
 SHAPES = [
     ("tiny_fp32", 128, 512, F32, 128, 16, 101),
     ("g64_bf16", 40, 2048, BF16, 64, 16, 102),
-    ("e64_narrow_g32", 12, 4096, BF16, 32, 16, 31),
-    ("e64_narrow_g2", 6, 4096, BF16, 2, 8, 32),
-    ("e64_g8", 6, 4096, F32, 8, 16, 33),
-    ("e64_wide_g1024", 10, 4096, BF16, 1024, 16, 34),
-    ("e64_row_group", 6, 4096, BF16, 4096, 4, 35),
+    ("k4096_narrow_g32", 12, 4096, BF16, 32, 16, 31),
+    ("k4096_narrow_g2", 6, 4096, BF16, 2, 8, 32),
+    ("k4096_g8", 6, 4096, F32, 8, 16, 33),
+    ("k4096_wide_g1024", 10, 4096, BF16, 1024, 16, 34),
+    ("k4096_row_group", 6, 4096, BF16, 4096, 4, 35),
     ("ragged_k1000", 9, 1000, BF16, 8, 16, 36),
     ("ragged_k96", 7, 96, F32, 32, 4, 37),
     ("k2_min", 5, 2, F32, 2, 2, 38),
@@ -42,8 +42,9 @@ SHAPES = [
     ("two_waves_k8192", 6, 8192, BF16, 128, 16, 40),
     ("two_waves_group_spans_waves", 4, 8192, BF16, 8192, 16, 41),
     ("seven_waves_k14336", 5, 14336, BF16, 128, 16, 42),
-    ("seven_waves_k28672", 3, 28672, BF16, 128, 16, 43),
-    ("four_waves_group_16384", 3, 16384, BF16, 16384, 8, 44),
+    ("fourteen_waves_k28672", 3, 28672, BF16, 128, 16, 43),
+    ("sixteen_waves_ragged_g2", 2, 32766, BF16, 2, 16, 46),
+    ("eight_waves_group_16384", 3, 16384, BF16, 16384, 8, 44),
     ("any2_k4096", 8, 4096, BF16, 128, 4, 45),
 ]
 

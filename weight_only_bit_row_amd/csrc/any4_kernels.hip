@@ -71,6 +71,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 constexpr int kMaxTrials = 4;
 __device__ __forceinline__ int greedy_trials(int k) { return k <= 2 ? 2 : (k == 4 ? 3 : 4); }
 
+constexpr int kMaxWaves = 16;  // waves per row: 1024-lane workgroups
+
 struct Smem {
   float c[kMaxClusters];      // centroids in draw order
   float thr[kMaxClusters + 4];       // switch points between sorted neighbours, +inf padded
@@ -78,17 +80,17 @@ struct Smem {
   float sv[kMaxClusters];     // sorted distinct centroid values
   int sidx[kMaxClusters];     // lowest draw index holding each sorted value
   union {
-    double wred[8][2 * kMaxClusters];   // per-wave partial bins (Lloyd rounds)
+    double wred[kMaxWaves][2 * kMaxClusters];   // per-wave partial bins (Lloyd rounds)
     struct {                            // greedy k-means++ (seeding)
       unsigned long long u[kMaxTrials - 1][kMaxClusters];  // draws of candidates 1..
-      unsigned long long pot[8][kMaxTrials];               // per-wave candidate potentials
+      unsigned long long pot[kMaxWaves][kMaxTrials];               // per-wave candidate potentials
       float cand_c[kMaxTrials];
       int cand_j[kMaxTrials];
     } gk;
   };
-  float fred[2][8];                     // per-wave fp32 partials (double buffered)
-  double dred[8];                       // per-wave fp64 partials
-  unsigned long long ured[2][8];        // per-wave u64 partials (double buffered)
+  float fred[2][kMaxWaves];                     // per-wave fp32 partials (double buffered)
+  double dred[kMaxWaves];                       // per-wave fp64 partials
+  unsigned long long ured[2][kMaxWaves];        // per-wave u64 partials (double buffered)
   unsigned long long u[kMaxClusters];   // Philox draw of each seeding step
   alignas(16) float stage_p[kWave];     // sampling weights of the lane owning a pick
   alignas(16) float stage_x[kWave];     // its scaled values
@@ -100,7 +102,7 @@ struct Smem {
   int pick_j;
   int n_unique;
   int use_table;                        // this round's cell table is complete
-  int bad[8];                           // per-wave vote: the row holds a bad value
+  int bad[kMaxWaves];                           // per-wave vote: the row holds a bad value
   int pad_[2];
 };
 
@@ -778,8 +780,7 @@ __device__ __forceinline__ double block_sum_f64(double v, Smem& S, int lane, int
 }
 
 // ---------------------------------------------------------------------------------
-// Occupancy target per element count: 32 elements per lane fit 3 waves per SIMD;
-// 64 do not (their registers would spill inside the Lloyd loop), so they get no hint.
+// Occupancy target per element count: 32 elements per lane fit 3 waves per SIMD.
 template <int E>
 struct WavesPerEU {
   static constexpr int value = (E == 32) ? 3 : 0;
@@ -793,9 +794,12 @@ struct WavesPerEU {
 // The variant instance for narrow groups is held to 2 waves per SIMD instead of 3: at
 // 168 VGPRs it spilled ~3700 registers around the narrow-group scaling cases; at 2 waves
 // it spills none and runs 17-35% faster (group 8 and 16 variants on 14336 x 4096).
+// Rows of 9 to 16 waves (NWMAX 16) fill a CU alone: a 1024-lane workgroup puts 4 waves on
+// every SIMD, which caps them at 128 VGPRs.
 template <int E, int NWMAX, int MODE, bool WIDE, bool VAR>
 __global__ __launch_bounds__(kWave* NWMAX)
-__attribute__((amdgpu_waves_per_eu((VAR && !WIDE && WavesPerEU<E>::value > 2)
+__attribute__((amdgpu_waves_per_eu(NWMAX > 8 ? 4
+                                   : (VAR && !WIDE && WavesPerEU<E>::value > 2)
                                        ? 2
                                        : (WavesPerEU<E>::value == 0 ? 1 : WavesPerEU<E>::value))))
 void any4_rows_kernel(const LaunchArgs args) {
@@ -1271,14 +1275,16 @@ hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipSt
 
 }  // namespace
 
-// Launch geometry for a row length, from measurements on the 14336 x 4096 workload:
-// 32 elements per lane (several waves per row) beat one 64-element wave per row,
-// whose register file allows only one wave per SIMD.
+// Launch geometry for a row length, from measurements: 32 elements per lane (several
+// waves per row) beat one 64-element wave per row on 14336 x 4096, whose register file
+// allows only one wave per SIMD.  Rows longer than 16384 keep 32 elements per lane on up
+// to 16 waves: against 64 elements on up to 8 waves (256 VGPRs, more spilled) they took
+// 7.7 ms instead of 8.3 on 8192 x 28672 and 3.0 instead of 3.9 on 4096 x 20480, with the
+// same output bits.
 RowConfig choose_config(int64_t K) {
   if (K <= 512) return {8, 1};
   if (K <= 1024) return {16, 1};
-  if (K <= 16384) return {32, static_cast<int>((K + 2047) / 2048)};
-  return {64, static_cast<int>((K + 4095) / 4096)};
+  return {32, static_cast<int>((K + 2047) / 2048)};
 }
 
 hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t n_blocks,
@@ -1289,15 +1295,14 @@ hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t 
       case 8: return launch_mode<8, 1>(args, mode, n_blocks, stream);
       case 16: return launch_mode<16, 1>(args, mode, n_blocks, stream);
       case 32: return launch_mode<32, 1>(args, mode, n_blocks, stream);
-      case 64: return launch_mode<64, 1>(args, mode, n_blocks, stream);
       default: return hipErrorInvalidValue;
     }
   }
+  if (cfg.nw > 8) return cfg.e == 32 ? launch_mode<32, 16>(args, mode, n_blocks, stream) : hipErrorInvalidValue;
   switch (cfg.e) {
     case 8: return launch_mode<8, 8>(args, mode, n_blocks, stream);
     case 16: return launch_mode<16, 8>(args, mode, n_blocks, stream);
     case 32: return launch_mode<32, 8>(args, mode, n_blocks, stream);
-    case 64: return launch_mode<64, 8>(args, mode, n_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -9,7 +9,7 @@ namespace any4 {
 
 constexpr int kMaxMats = 8;       // matrices per launch (descriptors travel as kernel arguments)
 constexpr int kMaxClusters = 16;
-constexpr int kMaxCols = 32768;   // 8 waves x 64 lanes x 64 elements held in registers
+constexpr int kMaxCols = 32768;   // 16 waves x 64 lanes x 32 elements held in registers
 
 enum Mode : int { MODE_FULL = 0, MODE_SCALE = 1, MODE_SEED = 2, MODE_STEP = 3 };
 
