@@ -40,13 +40,15 @@ VARIANTS = [
     ("symmetric_greedy_none", SYM | I_GREEDY | W_NONE),
 ]
 
-# (name, N, K, dtype, group, n_clusters, seed): wide and narrow groups, any1..any3, seven waves
+# (name, N, K, dtype, group, n_clusters, seed): wide and narrow groups, any1..any3, seven
+# waves, and twelve waves with narrow groups (the 1024-lane instance)
 SHAPES = [
     ("g128_k4096", 24, 4096, BF16, 128, 16, 201),
     ("narrow_g8_k1000", 9, 1000, BF16, 8, 16, 202),
     ("any2_g64_k512_f32", 12, 512, F32, 64, 4, 203),
     ("any3_k14336", 4, 14336, BF16, 128, 8, 204),
     ("any1_g32_k768", 10, 768, BF16, 32, 2, 206),
+    ("narrow_g16_k24576", 2, 24576, BF16, 16, 16, 207),
 ]
 
 

@@ -16,9 +16,9 @@
 //              Philox4x32-10 draw per (row, step)
 //   Lloyd      per round: sort the <=16 centroids, merge equal values (lowest draw
 //              index kept), compute the exact fp32 switch point between each pair of
-//              sorted neighbours, and tabulate them over fixed 1/32-wide cells of the
-//              scaled range (per cell, 8 bytes: cluster position at the cell start and
-//              the switch point inside it).  Each element's cell is fixed for the whole
+//              sorted neighbours, and tabulate them over 2k fixed cells, each half a
+//              scaled unit wide (per cell, 8 bytes: cluster position at the cell start
+//              and the switch point inside it).  Each element's cell is fixed for the whole
 //              row, so its E-step is one 8-byte LDS read and one compare; a round whose
 //              table would need a second switch point in one cell uses a 4-level
 //              binary search over all switch points instead (same result).  The
