@@ -169,6 +169,22 @@ int any4_stage_seed(const any4_matrix* m, const any4_params* params, float* c0,
 int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const float* c_in,
                           uint8_t* assign, float* c_out, double* objective, hipStream_t stream);
 
+/* Sorted-row Lloyd, the Lloyd-Max form of the per-row 1-D clustering (Section 2.5;
+ * Lloyd 1982, Max 1960): `params->iters` rounds of Eq. 18 assignment and Eq. 23 update
+ * from the centroids c_in [N, n_clusters] fp32, writing c_out [N, n_clusters] fp32.
+ * Inputs are the scaled rows w_s [N, K] and sample weights a [N, K] (fp32, as written by
+ * any4_stage_scale; device pointers, not modified).  Each row is sorted once with fp64
+ * prefix sums of a and a*w_s; a round costs one binary search per switch point and
+ * two prefix differences per cluster instead of a pass over the row.  The assignment
+ * rule is the same as any4_quantize's, so the fixed points are too; the sums differ
+ * only in fp64 rounding order.  Uses m->n_rows and m->n_cols only (other fields
+ * ignored); params->group is checked but unused and the symmetric flag of
+ * params->variant selects the scaled range.  Rows of at most 4096 columns
+ * (ANY4_ERR_UNSUPPORTED beyond); ANY4_ERR_INVALID_ARG for a NULL pointer with
+ * n_rows > 0, n_cols < 2 or odd, or bad params.  Asynchronous on `stream`. */
+int any4_stage_lloyd_sorted(const any4_matrix* m, const any4_params* params, const float* w_s,
+                            const float* a, const float* c_in, float* c_out, hipStream_t stream);
+
 /* Emission only: codes, lut, scale, offset of `m` from assign [N,K] uint8,
  * c [N, n_clusters] fp32, alpha/beta [N, K/group] fp32 (Section 2.4.1 layout). */
 int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8_t* assign,

@@ -32,7 +32,7 @@ EXPORTED = [
     "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
-    "any4_stage_full",
+    "any4_stage_full", "any4_stage_lloyd_sorted",
     "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize", "any4_lut_gemv",
 ]
 
@@ -89,6 +89,7 @@ def lib():
         L.any4_stage_scale.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_seed.argtypes = [MP, PP, P, P, P]
         L.any4_stage_lloyd_step.argtypes = [MP, PP, P, P, P, P, P]
+        L.any4_stage_lloyd_sorted.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_pack.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
         L.any4_launch_geometry.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
@@ -431,6 +432,29 @@ def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16, variant=0):
                                        _ptr(c_out), _ptr(obj), _stream(w.device)),
            "any4_stage_lloyd_step")
     return assign, c_out, obj
+
+
+def stage_lloyd_sorted(w_s, a, c_in, n_clusters=16, iters=20, variant=0, group=128):
+    """Sorted-row Lloyd: ``iters`` rounds from c_in [N, n_clusters] on the scaled rows
+    w_s and sample weights a ([N, K] fp32, K <= 4096); returns c_out [N, n_clusters]."""
+    torch = _torch()
+    _require_gpu(w_s)
+    N, K = w_s.shape
+    w_s = w_s.contiguous().to(torch.float32)
+    a = a.contiguous().to(torch.float32)
+    c_in = c_in.contiguous().to(torch.float32)
+    if a.shape != (N, K) or c_in.shape != (N, n_clusters):
+        raise ValueError("a must be [N, K] and c_in [N, n_clusters]")
+    if a.device != w_s.device or c_in.device != w_s.device:
+        raise ValueError("w_s, a and c_in must be on one device")
+    c_out = torch.empty((N, n_clusters), dtype=torch.float32, device=w_s.device)
+    m = Any4Matrix()
+    m.n_rows, m.n_cols = N, K
+    p = params(group, n_clusters, iters, 0, variant)
+    _check(lib().any4_stage_lloyd_sorted(ctypes.byref(m), ctypes.byref(p), _ptr(w_s), _ptr(a),
+                                         _ptr(c_in), _ptr(c_out), _stream(w_s.device)),
+           "any4_stage_lloyd_sorted")
+    return c_out
 
 
 def stage_pack(n_rows, n_cols, assign, c, alpha, beta, group=128, n_clusters=16):

@@ -311,6 +311,27 @@ int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const
   return launch_one(make_args(params, 1, nullptr), d, any4::MODE_STEP, stream);
 }
 
+int any4_stage_lloyd_sorted(const any4_matrix* m, const any4_params* params, const float* w_s,
+                            const float* a, const float* c_in, float* c_out, hipStream_t stream) {
+  const int st = check_params(params);
+  if (st != ANY4_OK) return st;
+  if (!m || m->n_rows < 0 || m->n_cols < 2 || (m->n_cols & 1)) return ANY4_ERR_INVALID_ARG;
+  if (m->n_cols > any4::kSortedMaxCols || m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_rows == 0) return ANY4_OK;
+  if (!w_s || !a || !c_in || !c_out) return ANY4_ERR_INVALID_ARG;
+  any4::SortedDesc d{};
+  d.w_s = w_s;
+  d.a = a;
+  d.c_in = c_in;
+  d.c_out = c_out;
+  d.n_rows = m->n_rows;
+  d.n_cols = static_cast<int32_t>(m->n_cols);
+  d.n_clusters = params->n_clusters;
+  d.iters = params->iters;
+  d.symmetric = (params->variant & any4::kVarSymmetric) ? 1 : 0;
+  return any4::launch_sorted_lloyd(d, stream) == hipSuccess ? ANY4_OK : ANY4_ERR_HIP;
+}
+
 int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8_t* assign,
                     const float* c, const float* alpha, const float* beta, hipStream_t stream) {
   int st = check_params(params);

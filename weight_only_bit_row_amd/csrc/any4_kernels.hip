@@ -1239,6 +1239,155 @@ __global__ void restart_merge_kernel(MergeDesc d) {
   if (threadIdx.x == 0) d.best_obj[row] = cand;
 }
 
+// ---------------------------------------------------------------------------------
+// Sorted-row Lloyd (the Lloyd-Max form of Section 2.5's per-row 1-D clustering): the
+// row's (w_S, a) pairs are sorted by w_S once and fp64 prefix sums P0 = sum a and
+// P1 = sum a*w_S are taken in that order.  A round then needs, for the current
+// centroids, the same exact fp32 switch points as the register path (so the same
+// Eq. 18 assignment), one binary search per switch point, and two prefix differences
+// per cluster for the Eq. 23 sums; the update itself is the register path's.  The
+// row, its prefix sums and the per-thread scan totals live in LDS:
+//   [Smem][key: kp floats][a: kp floats][P0: K+1][P1: K+1][totals: 2 x 256] (fp64)
+// with kp the row length rounded up to a power of two (padding keys +inf, a 0).
+constexpr int kSortedThreads = 256;
+
+__global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
+  const int K = d.n_cols, kp = d.kp, k = d.n_clusters, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  float* key = reinterpret_cast<float*>(smem_raw + kSmemHdr);
+  float* wt = key + kp;
+  double* P0 = reinterpret_cast<double*>(wt + kp);
+  double* P1 = P0 + (K + 1);
+  double* tot = P1 + (K + 1);
+  const int64_t row = blockIdx.x;
+  const float* ws = d.w_s + row * K;
+  const float* ar = d.a + row * K;
+  for (int i = tid; i < kp; i += kSortedThreads) {
+    key[i] = i < K ? ws[i] : __builtin_huge_valf();
+    wt[i] = i < K ? ar[i] : 0.0f;
+  }
+  if (tid < k) S.c[tid] = d.c_in[row * k + tid];
+  __syncthreads();
+  // bitonic sort, ascending by key; each step pairs lo and lo + stride inside blocks of
+  // 2 * stride, the direction set by the bit `size` of lo.  A thread's pairs of a step
+  // (pair i = tid + 256 r) are all loaded before any is compared and stored, so their
+  // LDS reads are in flight together; every index belongs to one pair per step.
+  constexpr int PER = kSortedMaxCols / 2 / kSortedThreads;
+  const int half = kp / 2;
+  for (int size = 2; size <= kp; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      float k0[PER], k1[PER], w0[PER], w1[PER];
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int i = tid + r * kSortedThreads;
+        if (i < half) {
+          const int lo = 2 * i - (i & (stride - 1));
+          k0[r] = key[lo];
+          k1[r] = key[lo + stride];
+          w0[r] = wt[lo];
+          w1[r] = wt[lo + stride];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int i = tid + r * kSortedThreads;
+        if (i < half) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const bool up = (lo & size) == 0;
+          if (up ? (k1[r] < k0[r]) : (k0[r] < k1[r])) {
+            key[lo] = k1[r];
+            key[lo + stride] = k0[r];
+            wt[lo] = w1[r];
+            wt[lo + stride] = w0[r];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // fp64 prefix sums in sorted order: each thread runs a contiguous chunk, the chunk
+  // totals are scanned by thread 0 in thread order, and the chunks are then rewritten
+  // from their base (one fixed order, so the sums are deterministic)
+  const int C = (K + kSortedThreads - 1) / kSortedThreads;
+  const int b0 = min(K, tid * C), b1 = min(K, b0 + C);
+  double s0 = 0.0, s1 = 0.0;
+  for (int i = b0; i < b1; ++i) {
+    const double av = wt[i];
+    s0 += av;
+    s1 += av * static_cast<double>(key[i]);
+  }
+  tot[tid] = s0;
+  tot[kSortedThreads + tid] = s1;
+  __syncthreads();
+  if (tid == 0) {
+    double r0 = 0.0, r1 = 0.0;
+    for (int t = 0; t < kSortedThreads; ++t) {
+      const double v0 = tot[t], v1 = tot[kSortedThreads + t];
+      tot[t] = r0;
+      tot[kSortedThreads + t] = r1;
+      r0 += v0;
+      r1 += v1;
+    }
+    P0[0] = 0.0;
+    P1[0] = 0.0;
+  }
+  __syncthreads();
+  {
+    double r0 = tot[tid], r1 = tot[kSortedThreads + tid];
+    for (int i = b0; i < b1; ++i) {
+      const double av = wt[i];
+      r0 += av;
+      r1 += av * static_cast<double>(key[i]);
+      P0[i + 1] = r0;
+      P1[i + 1] = r1;
+    }
+  }
+  __syncthreads();
+  // the rounds run on wave 0 alone (no block barrier from here on)
+  if (tid >= kWave) return;
+  const float off = d.symmetric ? static_cast<float>(k / 2) : 0.0f;
+  const int G = kCellsPerUnit * k;
+  float sv, t;
+  int si;
+  uint32_t tc;
+  int U = build_structure(S, k, G, off, lane, t, tc, sv, si);
+  for (int it = 0; it < d.iters; ++it) {
+    // lane p < U - 1: the number of keys below switch point p (elements at or above it
+    // sit right of sorted position p, the register path's rule)
+    int idx = K;
+    if (lane + 1 < U) {
+      const float th = S.thr[lane];
+      int lo = 0, hi = K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (key[mid] < th)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      idx = lo;
+    }
+    const int below = __shfl_up(idx, 1);
+    const int from = (lane == 0) ? 0 : below;
+    int to = (lane + 1 < U) ? idx : K;
+    if (to < from) to = from;
+    if (lane < kMaxClusters) {
+      double c0 = 0.0, c1 = 0.0;
+      if (lane < U) {
+        c0 = P0[to] - P0[from];
+        c1 = P1[to] - P1[from];
+      }
+      S.wred[0][lane] = c0;
+      S.wred[0][kMaxClusters + lane] = c1;
+    }
+    wave_lds_fence();
+    U = update_and_structure(S, 1, k, G, off, lane, U, sv, si, t, tc);
+  }
+  if (lane < k) d.c_out[row * k + lane] = S.c[lane];
+}
+
 template <int E, int NWMAX, int MODE>
 void launch_kernel(const LaunchArgs& args, dim3 grid, dim3 block, size_t smem, hipStream_t stream,
                    bool wide, bool var) {
@@ -1311,6 +1460,23 @@ hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
   hipLaunchKernelGGL(restart_merge_kernel, dim3(static_cast<unsigned>(d.n_rows)), dim3(256), 0,
                      stream, d);
+  return hipGetLastError();
+}
+
+size_t sorted_lloyd_lds_bytes(int64_t n_cols) {
+  int64_t kp = 2;
+  while (kp < n_cols) kp <<= 1;
+  return kSmemHdr + 2 * sizeof(float) * static_cast<size_t>(kp) +
+         2 * sizeof(double) * static_cast<size_t>(n_cols + 1) + 2 * sizeof(double) * kSortedThreads;
+}
+
+hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
+  if (d.n_rows == 0) return hipSuccess;
+  int kp = 2;
+  while (kp < d.n_cols) kp <<= 1;
+  d.kp = kp;
+  hipLaunchKernelGGL(sorted_lloyd_kernel, dim3(static_cast<unsigned>(d.n_rows)), dim3(kSortedThreads),
+                     sorted_lloyd_lds_bytes(d.n_cols), stream, d);
   return hipGetLastError();
 }
 

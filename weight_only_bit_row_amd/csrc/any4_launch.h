@@ -77,6 +77,27 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_t* assign,
                        const float* c, const float* alpha, const float* beta, hipStream_t stream);
 
+// Sorted-row Lloyd rounds behind any4_stage_lloyd_sorted: from the scaled rows w_s and
+// sample weights a ([n_rows, n_cols] fp32 each) and the centroids c_in [n_rows, k], run
+// `iters` rounds and write c_out [n_rows, k].  One 256-lane workgroup per row, the row
+// sorted in LDS, so rows hold at most kSortedMaxCols columns.
+constexpr int kSortedMaxCols = 4096;
+struct SortedDesc {
+  const float* w_s;
+  const float* a;
+  const float* c_in;
+  float* c_out;
+  int64_t n_rows;
+  int32_t n_cols;
+  int32_t kp;          // n_cols rounded up to a power of two (set by the launcher)
+  int32_t n_clusters;
+  int32_t iters;
+  int32_t symmetric;   // symmetric scaling: w_S in [-k/2, k/2]
+  int32_t pad_;
+};
+size_t sorted_lloyd_lds_bytes(int64_t n_cols);
+hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream);
+
 // Restarts: after restart r has written its outputs to the `cand_*` buffers, keep them
 // for every row whose objective is below the best so far (the earlier restart wins ties).
 struct MergeDesc {
