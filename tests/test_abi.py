@@ -182,6 +182,25 @@ def test_lut_gemv_validates_before_launch(L):
     m0.n_rows, m0.n_cols = 0, 256
     assert gemv(ctypes.byref(m0), ctypes.byref(p), None, 1, 1, None, None) == 0
 
+def test_sorted_lloyd_validates_before_launch(L):
+    """any4_stage_lloyd_sorted rejects bad params, missing buffers and odd or short rows
+    (invalid argument) and rows over 4096 columns (unsupported) without a HIP call; an
+    empty matrix is a no-op."""
+    p = any4.params(128, 16, 20, 0)
+    f = L.any4_stage_lloyd_sorted
+    buf = 0x8000
+    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), None, buf, buf, buf, None) == 1
+    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), buf, buf, buf, None, None) == 1
+    assert f(ctypes.byref(_mat(k=511)), ctypes.byref(p), buf, buf, buf, buf, None) == 1
+    assert f(ctypes.byref(_mat(k=0)), ctypes.byref(p), buf, buf, buf, buf, None) == 1
+    assert f(None, ctypes.byref(p), buf, buf, buf, buf, None) == 1
+    assert f(ctypes.byref(_mat(k=512)), ctypes.byref(any4.params(128, 5)), buf, buf, buf, buf, None) == 1
+    assert f(ctypes.byref(_mat(k=4098)), ctypes.byref(p), buf, buf, buf, buf, None) == 2
+    m0 = any4.Any4Matrix()
+    m0.n_rows, m0.n_cols = 0, 256
+    assert f(ctypes.byref(m0), ctypes.byref(p), None, None, None, None, None) == 0
+
+
 def test_launch_geometry(L):
     assert any4.launch_geometry(4096) == (32, 2)
     assert any4.launch_geometry(512) == (8, 1)
