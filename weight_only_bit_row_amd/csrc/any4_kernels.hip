@@ -1246,9 +1246,11 @@ __global__ void restart_merge_kernel(MergeDesc d) {
 // centroids, the same exact fp32 switch points as the register path (so the same
 // Eq. 18 assignment), one binary search per switch point, and two prefix differences
 // per cluster for the Eq. 23 sums; the update itself is the register path's.  The
-// row, its prefix sums and the per-thread scan totals live in LDS:
-//   [Smem][key: kp floats][a: kp floats][P0: K+1][P1: K+1][totals: 2 x 256] (fp64)
-// with kp the row length rounded up to a power of two (padding keys +inf, a 0).
+// sorted row and the prefix sums at the starts of its 256 chunks live in LDS:
+//   [Smem][key: kp floats][a: kp floats][chunk bases: 2 x 257 fp64]
+// with kp the row length rounded up to a power of two (padding keys +inf, a 0); a
+// prefix sum inside a chunk is its base plus that chunk's elements added in order.
+// ~40 KB at 4096 columns, so three rows share a CU.
 constexpr int kSortedThreads = 256;
 
 __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
@@ -1258,9 +1260,8 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
   const int lane = tid & (kWave - 1);
   float* key = reinterpret_cast<float*>(smem_raw + kSmemHdr);
   float* wt = key + kp;
-  double* P0 = reinterpret_cast<double*>(wt + kp);
-  double* P1 = P0 + (K + 1);
-  double* tot = P1 + (K + 1);
+  double* tot = reinterpret_cast<double*>(wt + kp);  // [2][kSortedThreads + 1]
+  constexpr int TB = kSortedThreads + 1;
   const int64_t row = blockIdx.x;
   const float* ws = d.w_s + row * K;
   const float* ar = d.a + row * K;
@@ -1307,42 +1308,34 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
       __syncthreads();
     }
   }
-  // fp64 prefix sums in sorted order: each thread runs a contiguous chunk, the chunk
-  // totals are scanned by thread 0 in thread order, and the chunks are then rewritten
-  // from their base (one fixed order, so the sums are deterministic)
+  // fp64 prefix sums in sorted order: thread t sums chunk t (C consecutive elements, in
+  // order), thread 0 turns the chunk totals into chunk bases in thread order, and
+  // P(i) = base of chunk i / C plus the chunk's elements before i, added in order (one
+  // fixed order, so the sums are deterministic)
   const int C = (K + kSortedThreads - 1) / kSortedThreads;
-  const int b0 = min(K, tid * C), b1 = min(K, b0 + C);
-  double s0 = 0.0, s1 = 0.0;
-  for (int i = b0; i < b1; ++i) {
-    const double av = wt[i];
-    s0 += av;
-    s1 += av * static_cast<double>(key[i]);
+  {
+    const int b0 = min(K, tid * C), b1 = min(K, b0 + C);
+    double s0 = 0.0, s1 = 0.0;
+    for (int i = b0; i < b1; ++i) {
+      const double av = wt[i];
+      s0 += av;
+      s1 += av * static_cast<double>(key[i]);
+    }
+    tot[tid] = s0;
+    tot[TB + tid] = s1;
   }
-  tot[tid] = s0;
-  tot[kSortedThreads + tid] = s1;
   __syncthreads();
   if (tid == 0) {
     double r0 = 0.0, r1 = 0.0;
     for (int t = 0; t < kSortedThreads; ++t) {
-      const double v0 = tot[t], v1 = tot[kSortedThreads + t];
+      const double v0 = tot[t], v1 = tot[TB + t];
       tot[t] = r0;
-      tot[kSortedThreads + t] = r1;
+      tot[TB + t] = r1;
       r0 += v0;
       r1 += v1;
     }
-    P0[0] = 0.0;
-    P1[0] = 0.0;
-  }
-  __syncthreads();
-  {
-    double r0 = tot[tid], r1 = tot[kSortedThreads + tid];
-    for (int i = b0; i < b1; ++i) {
-      const double av = wt[i];
-      r0 += av;
-      r1 += av * static_cast<double>(key[i]);
-      P0[i + 1] = r0;
-      P1[i + 1] = r1;
-    }
+    tot[kSortedThreads] = r0;
+    tot[TB + kSortedThreads] = r1;
   }
   __syncthreads();
   // the rounds run on wave 0 alone (no block barrier from here on)
@@ -1369,15 +1362,26 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
       }
       idx = lo;
     }
-    const int below = __shfl_up(idx, 1);
-    const int from = (lane == 0) ? 0 : below;
-    int to = (lane + 1 < U) ? idx : K;
-    if (to < from) to = from;
+    // prefix sums at the switch index (lane p < U - 1) or at K (the last position)
+    double q0 = 0.0, q1 = 0.0;
+    if (lane < U) {
+      const int at = (lane + 1 < U) ? idx : K;
+      const int ch = min(at / C, kSortedThreads);
+      q0 = tot[ch];
+      q1 = tot[TB + ch];
+      for (int i = ch * C; i < at; ++i) {
+        const double av = wt[i];
+        q0 += av;
+        q1 += av * static_cast<double>(key[i]);
+      }
+    }
+    const double p0 = __shfl_up(q0, 1), p1 = __shfl_up(q1, 1);
     if (lane < kMaxClusters) {
       double c0 = 0.0, c1 = 0.0;
       if (lane < U) {
-        c0 = P0[to] - P0[from];
-        c1 = P1[to] - P1[from];
+        c0 = (lane == 0) ? q0 : q0 - p0;
+        c1 = (lane == 0) ? q1 : q1 - p1;
+        if (!(c0 > 0.0)) c0 = c1 = 0.0;  // an empty range (or an unordered pair) adds nothing
       }
       S.wred[0][lane] = c0;
       S.wred[0][kMaxClusters + lane] = c1;
@@ -1466,8 +1470,7 @@ hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t stream) {
 size_t sorted_lloyd_lds_bytes(int64_t n_cols) {
   int64_t kp = 2;
   while (kp < n_cols) kp <<= 1;
-  return kSmemHdr + 2 * sizeof(float) * static_cast<size_t>(kp) +
-         2 * sizeof(double) * static_cast<size_t>(n_cols + 1) + 2 * sizeof(double) * kSortedThreads;
+  return kSmemHdr + 2 * sizeof(float) * static_cast<size_t>(kp) + 2 * sizeof(double) * (kSortedThreads + 1);
 }
 
 hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
