@@ -1252,6 +1252,51 @@ __global__ void restart_merge_kernel(MergeDesc d) {
 // prefix sum inside a chunk is its base plus that chunk's elements added in order.
 // ~40 KB at 4096 columns, so three rows share a CU.
 constexpr int kSortedThreads = 256;
+constexpr int kSortedRegs = 16;  // consecutive elements per thread in the register steps
+
+// One bitonic step of stride STRIDE < kSortedRegs on a thread's kSortedRegs consecutive
+// elements starting at index `base`: the same comparator as the LDS steps (ascending
+// where bit `size` of the lower index is clear), so the network and its result are
+// unchanged.
+template <int STRIDE>
+__device__ __forceinline__ void sort_step_regs(float (&kr)[kSortedRegs], float (&wr)[kSortedRegs], int base,
+                                               int size) {
+#pragma unroll
+  for (int j = 0; j < kSortedRegs; ++j) {
+    if ((j & STRIDE) == 0) {
+      const bool up = ((base + j) & size) == 0;
+      const float a = kr[j], b = kr[j + STRIDE];
+      const bool sw = up ? (b < a) : (a < b);
+      const float wa = wr[j], wb = wr[j + STRIDE];
+      kr[j] = sw ? b : a;
+      kr[j + STRIDE] = sw ? a : b;
+      wr[j] = sw ? wb : wa;
+      wr[j + STRIDE] = sw ? wa : wb;
+    }
+  }
+}
+
+// The steps of one `size` with strides 8, 4, 2, 1 (those below `size`), in registers.
+__device__ __forceinline__ void sort_small_strides(float* key, float* wt, int tid, int size) {
+  float kr[kSortedRegs], wr[kSortedRegs];
+  const int base = tid * kSortedRegs;
+#pragma unroll
+  for (int v = 0; v < kSortedRegs / 4; ++v) {
+    const float4 a = reinterpret_cast<const float4*>(key + base)[v];
+    const float4 b = reinterpret_cast<const float4*>(wt + base)[v];
+    kr[4 * v] = a.x; kr[4 * v + 1] = a.y; kr[4 * v + 2] = a.z; kr[4 * v + 3] = a.w;
+    wr[4 * v] = b.x; wr[4 * v + 1] = b.y; wr[4 * v + 2] = b.z; wr[4 * v + 3] = b.w;
+  }
+  if (size > 8) sort_step_regs<8>(kr, wr, base, size);
+  if (size > 4) sort_step_regs<4>(kr, wr, base, size);
+  if (size > 2) sort_step_regs<2>(kr, wr, base, size);
+  sort_step_regs<1>(kr, wr, base, size);
+#pragma unroll
+  for (int v = 0; v < kSortedRegs / 4; ++v) {
+    reinterpret_cast<float4*>(key + base)[v] = make_float4(kr[4 * v], kr[4 * v + 1], kr[4 * v + 2], kr[4 * v + 3]);
+    reinterpret_cast<float4*>(wt + base)[v] = make_float4(wr[4 * v], wr[4 * v + 1], wr[4 * v + 2], wr[4 * v + 3]);
+  }
+}
 
 __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -1275,10 +1320,25 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
   // 2 * stride, the direction set by the bit `size` of lo.  A thread's pairs of a step
   // (pair i = tid + 256 r) are all loaded before any is compared and stored, so their
   // LDS reads are in flight together; every index belongs to one pair per step.
+  // With kSortedRegs elements per thread (kp = 4096), the steps of stride below
+  // kSortedRegs stay inside a thread's consecutive elements and run in registers.
   constexpr int PER = kSortedMaxCols / 2 / kSortedThreads;
   const int half = kp / 2;
+  const bool regs = kp == kSortedThreads * kSortedRegs;
   for (int size = 2; size <= kp; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    if (regs && size <= kSortedRegs) {
+      if (size == kSortedRegs) {
+        // sizes 2 .. 16 together: a thread's 16 elements hold whole blocks of each
+        for (int sz = 2; sz <= kSortedRegs; sz <<= 1) {
+          if (sz > 2) __syncthreads();
+          sort_small_strides(key, wt, tid, sz);
+        }
+        __syncthreads();
+      }
+      continue;
+    }
+    const int last = regs ? kSortedRegs : 1;  // smallest stride taken in LDS
+    for (int stride = size >> 1; stride >= last; stride >>= 1) {
       float k0[PER], k1[PER], w0[PER], w1[PER];
 #pragma unroll
       for (int r = 0; r < PER; ++r) {
@@ -1305,6 +1365,10 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
           }
         }
       }
+      __syncthreads();
+    }
+    if (regs) {
+      sort_small_strides(key, wt, tid, size);
       __syncthreads();
     }
   }
