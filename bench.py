@@ -10,10 +10,12 @@ outputs are preallocated.  Prints ONE JSON line.
   python bench.py --profile-steps 2 --iters 0   # same, without Lloyd rounds (counter deltas)
   python bench.py --copy-calibration         # plain copy of known size (counter scale)
   python bench.py --bookends-only --profile-steps 5   # only E|x| and dequantization
+  python bench.py --sorted-only --profile-steps 5     # only the sorted-row Lloyd stage
 
 The same line reports the two bookend kernels (E|x| of a calibration batch and the
 Eq. 4 dequantization of the quantized matrix) against the HBM roofline under
-"bookends"; they run after the timed quantizer steps and are not part of `value`.
+"bookends", and the sorted-row Lloyd stage on the same matrix under "sorted_lloyd";
+they run after the timed quantizer steps and are not part of `value`.
 """
 from __future__ import annotations
 
@@ -108,6 +110,29 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, stream, n_launches=10):
+    """The sorted-row Lloyd stage on the same matrix: scaled rows, sample weights and
+    k-means++ centres from the GPU stages, then `iters` rounds, and 0 rounds (sort and
+    prefix sums only), each the mean over a batch of launches with HIP events on the
+    launch stream.  `rows_identical` compares its centroids with the register path's."""
+    ws_, _, _, a = any4.stage_scale(w, act, group=g, n_clusters=k)
+    c0, _ = any4.stage_seed(w, act, group=g, n_clusters=k)
+    res = {"kernel": "sorted_lloyd_kernel", "n_rows": int(w.shape[0]), "n_cols": int(w.shape[1])}
+    for n_it in (0, iters):
+        c = any4.stage_lloyd_sorted(ws_, a, c0, n_clusters=k, iters=n_it, group=g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_launches):
+            any4.stage_lloyd_sorted(ws_, a, c0, n_clusters=k, iters=n_it, group=g)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["ms_rounds_%d" % n_it] = e0.elapsed_time(e1) / n_launches
+    res["rows_identical_with_register_path"] = float(
+        (c.view(torch.int32) == c_reg.view(torch.int32)).all(dim=1).float().mean().item())
+    return res
 
 
 def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
@@ -243,6 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bookends", action="store_true",
                     help="skip the E|x|, dequant and LUT matrix-vector kernels")
+    ap.add_argument("--sorted-only", action="store_true",
+                    help="only the sorted-row Lloyd stage (with --profile-steps: launches per size)")
     ap.add_argument("--bookends-only", action="store_true",
                     help="with --profile-steps: run only the E|x|, dequant and LUT matrix-vector kernels")
     args = ap.parse_args()
@@ -271,6 +298,13 @@ def main():
     out = any4.quantize(w, act, group=g, n_clusters=k, iters=iters)   # allocates outputs
     ws = any4.workspace(dev)
     torch.cuda.synchronize()
+
+    if args.sorted_only:
+        _, c_reg, _, _ = any4.stage_full(w, act, g, k, iters, seed=0)
+        res = sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, torch.cuda.current_stream(dev),
+                           n_launches=args.profile_steps or 10)
+        print(json.dumps({"sorted_lloyd": res}))
+        return
 
     if args.profile_steps and args.bookends_only:
         bookends(any4, torch, np, out, N, K, g, k, dev, torch.cuda.current_stream(dev),
@@ -352,6 +386,8 @@ def main():
     }
     if not args.no_bookends:
         line["bookends"] = bookends(any4, torch, np, out, N, K, g, k, dev, stream)
+        _, c_reg, _, _ = any4.stage_full(w, act, g, k, iters, seed=0)
+        line["sorted_lloyd"] = sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(m, g, k, iters)
     print(json.dumps(line))
