@@ -181,7 +181,9 @@ int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const
  * ignored); params->group is checked but unused and the symmetric flag of
  * params->variant selects the scaled range.  Rows of at most 4096 columns
  * (ANY4_ERR_UNSUPPORTED beyond); ANY4_ERR_INVALID_ARG for a NULL pointer with
- * n_rows > 0, n_cols < 2 or odd, or bad params.  Asynchronous on `stream`. */
+ * n_rows > 0, n_cols < 2 or odd, or bad params.  A row holding a non-finite w_s or a
+ * (which any4_stage_scale reports through its status) gives unspecified centroids for
+ * that row only.  The caller owns every buffer.  Asynchronous on `stream`. */
 int any4_stage_lloyd_sorted(const any4_matrix* m, const any4_params* params, const float* w_s,
                             const float* a, const float* c_in, float* c_out, hipStream_t stream);
 
