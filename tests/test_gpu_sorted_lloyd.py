@@ -76,6 +76,28 @@ def test_sorted_lloyd_matches_oracle(shape):
     assert same.mean() >= 0.75
 
 
+def test_sorted_lloyd_rows_of_few_distinct_values():
+    """Rows holding only 3 to 6 distinct values: runs of equal keys in the sorted row,
+    empty clusters and centroids that merge (fewer distinct centroids than k)."""
+    rng = np.random.default_rng(320)
+    N, K, g, k = 6, 1024, 128, 16
+    w = np.stack([rng.choice(rng.normal(0, 0.02, size=3 + i % 4).astype(np.float32), size=K)
+                  for i in range(N)]).astype(np.float32)
+    act = rng.lognormal(0, 0.5, size=K).astype(np.float32)
+
+    class M:
+        pass
+    m = M()
+    m.w, m.dtype, m.act = w, F32, act
+    ws, a, c0 = oracle_inputs(m, g, k, 0, 5)
+    dev = torch.device("cuda")
+    c_gpu = any4().stage_lloyd_sorted(torch.from_numpy(ws).to(dev), torch.from_numpy(a).to(dev),
+                                      torch.from_numpy(c0).to(dev), n_clusters=k, iters=20).cpu().numpy()
+    for i in range(N):
+        c_ref, _, _ = oracle.lloyd_row(ws[i], a[i], c0[i], 20)
+        assert np.array_equal(c_gpu[i].view(np.uint32), c_ref.view(np.uint32)), i
+
+
 def test_sorted_lloyd_zero_rounds_returns_the_start():
     m = make_matrix("zero", 4, 256, BF16, 310)
     ws, a, c0 = oracle_inputs(m, 128, 16, 0, 0)
