@@ -597,6 +597,23 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], const
 }
 
 // ---------------------------------------------------------------------------------
+// The k-means++ sampling weights of a lane's E elements: in registers, or, for rows of
+// 9-16 waves (1024-lane workgroups, 128 VGPRs, where they would spill), in the wave's
+// bin area, which seeding does not use (element m of lane l at word m * 64 + l, so a
+// wave's accesses to one m hit 64 consecutive words).
+template <int E, bool IN_LDS>
+struct SeedWeights {
+  float r[IN_LDS ? 1 : E];
+  float* l;
+  __device__ __forceinline__ float& operator[](int m) {
+    if constexpr (IN_LDS)
+      return l[m * kWave];
+    else
+      return r[m];
+  }
+};
+
+// ---------------------------------------------------------------------------------
 // One pass over the lane's elements with the current centroids.  The cluster
 // position comes from the cell table (TABLE) or the binary search; ACCUM adds the two
 // Eq. 23 sums into lane-private fp64 bins (address pos*64 + lane: conflict-free;
@@ -934,7 +951,10 @@ void any4_rows_kernel(const LaunchArgs args) {
       philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
       S.gk.u[s - 1][t] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
     }
-    float pv[E];
+    constexpr bool kPvLds = NWMAX > 8 && !VAR;
+    static_assert(!kPvLds || E * kWave * sizeof(float) <= kBinBytesPerWave, "weights fit the bins");
+    SeedWeights<E, kPvLds> pv;
+    pv.l = reinterpret_cast<float*>(smem_raw + kSmemHdr + kTableBytes + wave * kBinBytesPerWave) + lane;
     float lmax = 0.0f;  // this lane's largest sampling weight for the coming draw
 #pragma unroll
     for (int m = 0; m < E; ++m) {
@@ -1472,7 +1492,8 @@ void launch_kernel(const LaunchArgs& args, dim3 grid, dim3 block, size_t smem, h
 template <int E, int NWMAX>
 hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream) {
   const int nw = (NWMAX == 1) ? 1 : args.nw;
-  const size_t smem = kSmemHdr + ((mode == MODE_FULL || mode == MODE_STEP)
+  // the bin area also holds the sampling weights of 9-16-wave rows while they seed
+  const size_t smem = kSmemHdr + ((mode == MODE_FULL || mode == MODE_STEP || mode == MODE_SEED)
                                       ? kTableBytes + static_cast<size_t>(nw) * kBinBytesPerWave
                                       : 0);
   const dim3 grid(static_cast<unsigned>(n_blocks));
