@@ -951,7 +951,7 @@ void any4_rows_kernel(const LaunchArgs args) {
       philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
       S.gk.u[s - 1][t] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
     }
-    constexpr bool kPvLds = NWMAX > 8 && !VAR;
+    constexpr bool kPvLds = NWMAX > 8;
     static_assert(!kPvLds || E * kWave * sizeof(float) <= kBinBytesPerWave, "weights fit the bins");
     SeedWeights<E, kPvLds> pv;
     pv.l = reinterpret_cast<float*>(smem_raw + kSmemHdr + kTableBytes + wave * kBinBytesPerWave) + lane;
