@@ -598,7 +598,7 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], const
 
 // ---------------------------------------------------------------------------------
 // The k-means++ sampling weights of a lane's E elements: in registers, or, for rows of
-// 9-16 waves (1024-lane workgroups, 128 VGPRs, where they would spill), in the wave's
+// 5-16 waves (1024-lane workgroups, 128 VGPRs, where they would spill), in the wave's
 // bin area, which seeding does not use (element m of lane l at word m * 64 + l, so a
 // wave's accesses to one m hit 64 consecutive words).
 template <int E, bool IN_LDS>
@@ -811,8 +811,8 @@ struct WavesPerEU {
 // The variant instance for narrow groups is held to 2 waves per SIMD instead of 3: at
 // 168 VGPRs it spilled ~3700 registers around the narrow-group scaling cases; at 2 waves
 // it spills none and runs 17-35% faster (group 8 and 16 variants on 14336 x 4096).
-// Rows of 9 to 16 waves (NWMAX 16) fill a CU alone: a 1024-lane workgroup puts 4 waves on
-// every SIMD, which caps them at 128 VGPRs.
+// The 1024-lane instance (NWMAX 16, rows of 5 to 16 waves) is capped at 128 VGPRs: such a
+// workgroup may put 4 waves on every SIMD.
 template <int E, int NWMAX, int MODE, bool WIDE, bool VAR>
 __global__ __launch_bounds__(kWave* NWMAX)
 __attribute__((amdgpu_waves_per_eu(NWMAX > 8 ? 4
@@ -1536,7 +1536,10 @@ hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t 
       default: return hipErrorInvalidValue;
     }
   }
-  if (cfg.nw > 8) return cfg.e == 32 ? launch_mode<32, 16>(args, mode, n_blocks, stream) : hipErrorInvalidValue;
+  // rows of 5 or more waves take the 1024-lane instance: at 128 VGPRs (sampling weights
+  // in the bin area) two rows of 5-8 waves share a CU, 18-27% faster than one row at
+  // 168 VGPRs; rows of 2-4 waves already fill a CU and are not faster there
+  if (cfg.nw > 4) return cfg.e == 32 ? launch_mode<32, 16>(args, mode, n_blocks, stream) : hipErrorInvalidValue;
   switch (cfg.e) {
     case 8: return launch_mode<8, 8>(args, mode, n_blocks, stream);
     case 16: return launch_mode<16, 8>(args, mode, n_blocks, stream);
