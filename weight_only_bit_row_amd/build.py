@@ -1,9 +1,17 @@
-"""Build libany4.so (gfx950 kernels + C ABI) in-tree with hipcc."""
+"""Build libany4.so (gfx950 kernels + C ABI) in-tree with hipcc.
+
+Each source compiles to an object in a temporary directory, all in parallel (the row
+kernel's geometries are separate translation units), then one link step writes the
+library next to this file.
+"""
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,23 +26,51 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # correctly rounded fp32 division (scaling and the Eq. 23 update divide).
 # packed fp32 ops disabled.
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
 
-SOURCES = ["any4_kernels.hip", "any4_bookends.hip", "any4_api.cpp"]
+SOURCES = ["any4_rows_e32_w16.hip", "any4_rows_e32_w8.hip", "any4_rows_e32_w1.hip",
+           "any4_rows_e16.hip", "any4_rows_e8.hip", "any4_kernels.hip", "any4_bookends.hip",
+           "any4_api.cpp"]
+
+
+def _jobs() -> int:
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit():
+        return max(1, int(env))
+    return max(1, min(len(SOURCES), len(os.sched_getaffinity(0))))
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    tmpdir = tempfile.mkdtemp(prefix="any4_build_")
+    try:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+
+        def compile_one(i):
+            cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", objs[i],
+                   os.path.join(CSRC, SOURCES[i])]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            return r.returncode, cmd, r.stdout + r.stderr
+
+        with ThreadPoolExecutor(_jobs()) as ex:
+            results = list(ex.map(compile_one, range(len(SOURCES))))
+        for rc, cmd, out in results:
+            if rc != 0:
+                sys.stderr.write(out)
+                raise subprocess.CalledProcessError(rc, cmd)
+        tmp = LIB + ".tmp"
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -68,6 +68,13 @@ struct RowConfig {
 };
 RowConfig choose_config(int64_t n_cols);
 
+// Row-kernel instances, one translation unit each (any4_rows_e*.hip): 8 or 16
+// elements per lane on one wave, 32 on one wave, 2-4 waves, and 5-16 waves.
+hipError_t launch_rows_e8(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream);
+hipError_t launch_rows_e16(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream);
+hipError_t launch_rows_e32_w1(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream);
+hipError_t launch_rows_e32_w8(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream);
+hipError_t launch_rows_e32_w16(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream);
 // Launch one row kernel over all rows of args (args.nw must match cfg.nw).
 hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t n_blocks,
                        hipStream_t stream);
