@@ -198,6 +198,16 @@ int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8
 int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_final,
                     int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The batched path of any4_quantize (the same launches: one per row geometry over
+ * every matrix of the batch, longer rows first), additionally writing for each matrix
+ * i the fp32 centroids before the fp16 cast, c_final[i] [n_rows_i, n_clusters], and
+ * the k-means++ picks, picks[i] [n_rows_i, n_clusters] (of the restart that was kept).
+ * c_final and picks are host arrays of `count` device pointers; either array, or any
+ * of its entries, may be NULL.  Arguments, workspace and errors as any4_quantize. */
+int any4_stage_quantize_batch(const any4_matrix* mats, int32_t count, const any4_params* params,
+                              float* const* c_final, int32_t* const* picks, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* ---- bookends: the calibration statistic the quantizer consumes and the
  * dequantization of what it emits. ---- */
 

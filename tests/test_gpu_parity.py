@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import (OBJECTIVE_REL, centroid_close, excused_mismatch, say, to_device,
+from parity_util import (OBJECTIVE_REL, centroid_close, check_rows, excused_mismatch, say, to_device,
                          unpack_codes, widen)
 from workloads import BF16, F32, make, make_matrix
 
@@ -147,18 +147,13 @@ def test_t4_end_to_end(case):
     obj = out.objective.cpu().numpy()
     J, Jr = obj.sum(), ref["objective"].sum()
     assert abs(J - Jr) <= OBJECTIVE_REL * Jr, (J, Jr)
-    # per row: identical codes, or a trajectory that split at an excused near-tie
     codes = out.codes.cpu().numpy()
-    same_rows = (codes == ref["codes"]).all(axis=1)
     cf = c_final.cpu().numpy()
-    assert centroid_close(cf[same_rows], ref["c_final"][same_rows]).all()
-    assert same_rows.mean() >= 0.9, same_rows.mean()
+    lut = out.lut.cpu().numpy().view(np.uint16)
+    same_rows = check_rows(any4(), m, g, k, iters, 0, codes, cf, lut, ref, np.arange(m.w.shape[0]))
     # scale/offset do not depend on the clustering: bit-exact
     assert np.array_equal(out.scale.cpu().numpy().view(np.uint16), ref["scale"])
     assert np.array_equal(out.offset.cpu().numpy().view(np.uint16), ref["offset"])
-    lut = out.lut.cpu().numpy().view(np.uint16)
-    lut_same = (lut == ref["lut"]) | (np.abs(lut.astype(np.int32) - ref["lut"].astype(np.int32)) <= 1)
-    assert lut_same[same_rows].all()
     say(f"  {name}: rows with identical codes {same_rows.mean():.4f}, dJ/J {(J - Jr) / max(Jr, 1e-300):.2e}")
 
 
@@ -313,51 +308,67 @@ def test_batch_equals_single_calls():
 
 # ---- the named workloads at full size, on sampled rows ----------------------------------
 
-FULL = [("up_proj", 24), ("down_70b", 6), ("q_proj_g64", 24), ("q_proj_g128", 24)]
+FULL = [("up_proj", 32), ("down_70b", 32), ("q_proj_g64", 32), ("q_proj_g128", 32)]
+
+
+def _sample(N, n):
+    return np.unique(np.concatenate([[0, N - 1], np.linspace(0, N - 1, n).astype(int)]))
+
+
+def _check_sampled(m, out, cf, pk, g, k, iters, rows):
+    """The oracle on each sampled row alone (row_offset = its index keeps its Philox
+    stream): picks and scale/offset bit-exact, codes identical or explained, centroids
+    and LUT within tolerance, and the sampled rows' objective sum within 1e-4."""
+    codes, obj = out.codes.cpu().numpy(), out.objective.cpu().numpy()
+    lut = out.lut.cpu().numpy().view(np.uint16)
+    scale = out.scale.cpu().numpy().view(np.uint16)
+    offset = out.offset.cpu().numpy().view(np.uint16)
+    cf, pk = cf.cpu().numpy(), pk.cpu().numpy()
+    J = Jr = 0.0
+    same = np.zeros(rows.size, bool)
+    for n, i in enumerate(rows):
+        r = oracle.quantize(m.w[i:i + 1], m.dtype, m.act, g, k, iters, seed=0, row_offset=int(i),
+                            matrix_index=m.matrix_index)
+        assert r["status"] == 0
+        assert np.array_equal(pk[i], r["picks"][0]), (m.name, i, pk[i], r["picks"][0])
+        assert np.array_equal(scale[i], r["scale"][0]) and np.array_equal(offset[i], r["offset"][0]), (m.name, i)
+        same[n] = check_rows(any4(), m, g, k, iters, 0, codes, cf, lut, r, [i], [0], m.matrix_index)[0]
+        J += obj[i]
+        Jr += r["objective"][0]
+    assert abs(J - Jr) <= OBJECTIVE_REL * Jr, (m.name, J, Jr)
+    return same, (J - Jr) / Jr
 
 
 @pytest.mark.parametrize("wname,n_sample", FULL, ids=[f[0] for f in FULL])
 def test_full_size_sampled_rows(wname, n_sample):
     wl = make(wname)
     m = wl.matrices[0]
-    say(f"full-size {wname} {m.w.shape}: one launch over all rows, oracle on {n_sample} rows")
+    say(f"full-size {wname} {m.w.shape}: one launch over all rows, oracle on {n_sample}+ rows")
     w, act = to_device(m)
-    out = any4().quantize(w, act, group=wl.group, n_clusters=wl.n_clusters, iters=wl.iters, seed=0)
+    outs, cfs, pks, _ = any4().stage_quantize_batch([(w, act)], group=wl.group, n_clusters=wl.n_clusters,
+                                                    iters=wl.iters, seed=0)
     torch.cuda.synchronize()
-    N = m.w.shape[0]
-    rows = np.unique(np.linspace(0, N - 1, n_sample).astype(int))
-    codes, obj = out.codes.cpu().numpy(), out.objective.cpu().numpy()
-    lut = out.lut.cpu().numpy().view(np.uint16)
-    J = Jr = 0.0
-    same = 0
-    for i in rows:
-        r = oracle.quantize(m.w[i:i + 1], m.dtype, m.act, wl.group, wl.n_clusters, wl.iters, seed=0,
-                            row_offset=int(i))
-        J += obj[i]
-        Jr += r["objective"][0]
-        if np.array_equal(codes[i], r["codes"][0]):
-            same += 1
-            assert (np.abs(lut[i].astype(int) - r["lut"][0].astype(int)) <= 1).all()
-    assert abs(J - Jr) <= OBJECTIVE_REL * Jr, (J, Jr)
-    assert same >= 0.9 * rows.size
-    say(f"  {wname}: {same}/{rows.size} sampled rows identical, dJ/J {(J - Jr) / Jr:.2e}")
+    rows = _sample(m.w.shape[0], n_sample)
+    same, dj = _check_sampled(m, outs[0], cfs[0], pks[0], wl.group, wl.n_clusters, wl.iters, rows)
+    say(f"  {wname}: {same.sum()}/{rows.size} sampled rows identical, dJ/J {dj:.2e}")
 
 
 @pytest.mark.parametrize("bits", [4, 3, 2])
 def test_layer_batch_sampled_rows(bits):
+    """The 7 matrices of a decoder layer in one call (any4/any3/any2): on 64+ rows of
+    every matrix, including its first and last, picks, codes, LUT, scale and offset are
+    compared with the oracle row by row, which checks the launch's mapping of blocks to
+    matrices, rows, Philox counters and cluster counts."""
     wl = make(f"layer_any{bits}")
     say(f"layer any{bits}: one call over 7 matrices")
     dev = [to_device(m) for m in wl.matrices]
-    outs = any4().quantize_batch(dev, group=wl.group, n_clusters=wl.n_clusters, iters=wl.iters,
-                                 seed=0, matrix_indices=[m.matrix_index for m in wl.matrices])
+    outs, cfs, pks, ws = any4().stage_quantize_batch(dev, group=wl.group, n_clusters=wl.n_clusters,
+                                                     iters=wl.iters, seed=0,
+                                                     matrix_indices=[m.matrix_index for m in wl.matrices])
     torch.cuda.synchronize()
-    J = Jr = 0.0
-    for m, o in zip(wl.matrices, outs):
-        N = m.w.shape[0]
-        obj = o.objective.cpu().numpy()
-        for i in [0, N // 2, N - 1]:
-            r = oracle.quantize(m.w[i:i + 1], 1, m.act, wl.group, wl.n_clusters, wl.iters, seed=0,
-                                row_offset=i, matrix_index=m.matrix_index)
-            J += obj[i]
-            Jr += r["objective"][0]
-    assert abs(J - Jr) <= OBJECTIVE_REL * Jr, (J, Jr)
+    assert any4().read_status(ws) == 0
+    for m, o, cf, pk in zip(wl.matrices, outs, cfs, pks):
+        rows = _sample(m.w.shape[0], 64)
+        same, dj = _check_sampled(m, o, cf, pk, wl.group, wl.n_clusters, wl.iters, rows)
+        say(f"  any{bits} {m.name} {m.w.shape}: {same.sum()}/{rows.size} sampled rows identical, "
+            f"dJ/J {dj:.2e}")

@@ -2,8 +2,9 @@
 configurations (row count, row length up to 32768, group 2..256, 2..16 clusters, fp32 and
 bf16, 0..20 Lloyd rounds, every sample-weight / initialization / scaling variant, restarts),
 each judged like T4: both report a good status, the matrix objective agrees within 1e-4,
-at least 90% of rows have identical codes, and on those rows the picks are identical and the
-centroids within tolerance; scale and offset are bit-exact.
+the picks are identical, every row has identical codes (with centroids and LUT within
+tolerance) or a first divergence that is an excused near-tie or an in-tolerance M-step
+rounding (with restarts: identical rows only); scale and offset are bit-exact.
 """
 import json
 
@@ -11,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import OBJECTIVE_REL, centroid_close, say, to_device
+from parity_util import OBJECTIVE_REL, check_rows, say, to_device
 from workloads import BF16, F32, make_matrix
 
 pytestmark = pytest.mark.gpu
@@ -64,13 +65,14 @@ def test_random_configurations_match_the_oracle():
         J, Jr = out.objective.cpu().numpy().sum(), ref["objective"].sum()
         if not abs(J - Jr) <= OBJECTIVE_REL * max(Jr, 1e-30):
             problems.append(f"objective {J} vs {Jr}")
-        same = (out.codes.cpu().numpy() == ref["codes"]).all(axis=1)
-        if same.mean() < 0.9:
-            problems.append(f"identical rows {same.mean():.3f}")
-        if not np.array_equal(picks.cpu().numpy()[same], ref["picks"][same]):
+        if not np.array_equal(picks.cpu().numpy(), ref["picks"]):
             problems.append("picks")
-        if not centroid_close(c_final.cpu().numpy()[same], ref["c_final"][same]).all():
-            problems.append("centroids")
+        try:
+            check_rows(any4(), m, c["g"], c["k"], c["iters"], c["seed"], out.codes.cpu().numpy(),
+                       c_final.cpu().numpy(), out.lut.cpu().numpy().view(np.uint16), ref,
+                       np.arange(c["N"]), variant=c["variant"])
+        except AssertionError as e:
+            problems.append(f"rows: {e}")
         if not np.array_equal(out.scale.cpu().numpy().view(np.uint16), ref["scale"]):
             problems.append("scale")
         if not np.array_equal(out.offset.cpu().numpy().view(np.uint16), ref["offset"]):

@@ -2,16 +2,19 @@
 
 Each variant goes through the same protocol as the default path: scaling and sample
 weights bit-exact (T1), initial centres and picks bit-exact (T2), one Lloyd round from
-the oracle's centroids with assignments bit-exact except near-ties (T3, symmetric
-scaling, whose scaled weights are negative too), and the whole path (T4: picks exact,
-objective within 1e-4, >= 90% of rows with identical codes, scale/offset bit-exact).
-Restarts are checked end to end the same way, plus: never worse than one restart.
+the oracle's centroids with assignments bit-exact except near-ties and the M-step within
+tolerance (T3, for every variant that changes the scaled weights or the sample weights of
+Eq. 23), and the whole path (T4: picks exact, objective within 1e-4, every row's codes
+identical or its first divergence an excused near-tie or in-tolerance M-step rounding,
+scale/offset bit-exact).  Restarts are checked end to end the same way (every row
+identical), plus: never worse than one restart.
 """
 import numpy as np
 import pytest
 
 import oracle
-from parity_util import (OBJECTIVE_REL, centroid_close, excused_mismatch, say, to_device, widen)
+from parity_util import (OBJECTIVE_REL, centroid_close, check_rows, excused_mismatch, say, to_device,
+                         widen)
 from workloads import BF16, F32, make_matrix
 
 pytestmark = pytest.mark.gpu
@@ -99,8 +102,9 @@ def test_variant_seed_bit_exact(case):
 
 def test_variant_lloyd_round(case):
     name, m, g, k, variant = case
-    if not variant & SYM:
-        pytest.skip("the Lloyd round only changes with symmetric scaling (negative w_S)")
+    if not variant & (SYM | 3):
+        pytest.skip("initialization-only variant: a round from given centroids does not "
+                    "depend on how the first centroids were chosen")
     say(f"variant T3 {name}")
     ref = oracle.quantize(m.w, m.dtype, m.act, g, k, 6, trace=True, variant=variant)
     rows = oracle_rows(m, g, k, variant)
@@ -127,10 +131,10 @@ def _end_to_end(name, m, g, k, variant, iters=20):
     J, Jr = obj.sum(), ref["objective"].sum()
     assert abs(J - Jr) <= OBJECTIVE_REL * max(Jr, 1e-30), (J, Jr)
     codes = out.codes.cpu().numpy()
-    same = (codes == ref["codes"]).all(axis=1)
-    assert same.mean() >= 0.9, same.mean()
-    assert np.array_equal(picks.cpu().numpy()[same], ref["picks"][same])
-    assert centroid_close(c_final.cpu().numpy()[same], ref["c_final"][same]).all()
+    assert np.array_equal(picks.cpu().numpy(), ref["picks"])
+    same = check_rows(any4(), m, g, k, iters, 0, codes, c_final.cpu().numpy(),
+                      out.lut.cpu().numpy().view(np.uint16), ref, np.arange(m.w.shape[0]),
+                      variant=variant)
     assert np.array_equal(out.scale.cpu().numpy().view(np.uint16), ref["scale"])
     assert np.array_equal(out.offset.cpu().numpy().view(np.uint16), ref["offset"])
     say(f"  {name}: rows with identical codes {same.mean():.4f}, dJ/J {(J - Jr) / max(Jr, 1e-300):.2e}")

@@ -32,7 +32,7 @@ EXPORTED = [
     "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
-    "any4_stage_full", "any4_stage_lloyd_sorted",
+    "any4_stage_full", "any4_stage_lloyd_sorted", "any4_stage_quantize_batch",
     "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize", "any4_lut_gemv",
 ]
 
@@ -92,6 +92,7 @@ def lib():
         L.any4_stage_lloyd_sorted.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_pack.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
+        L.any4_stage_quantize_batch.argtypes = [MP, ctypes.c_int32, PP, P, P, P, ctypes.c_size_t, P]
         L.any4_launch_geometry.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
         L.any4_act_absmean_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
@@ -486,3 +487,30 @@ def stage_full(w, act, group=128, n_clusters=16, iters=20, seed=0, row_offset=0,
     _check(lib().any4_stage_full(ctypes.byref(m), ctypes.byref(p), _ptr(c_final), _ptr(picks),
                                  _ptr(ws), ws.numel(), _stream(w.device)), "any4_stage_full")
     return out, c_final, picks, ws
+
+
+def stage_quantize_batch(items, group=128, n_clusters=16, iters=20, seed=0, matrix_indices=None,
+                         variant=0):
+    """The batched path over several (W, act) pairs (one launch per row geometry, as
+    quantize_batch) plus, per matrix, the fp32 final centroids and the k-means++ picks.
+    Returns (outputs, c_finals, picks, ws)."""
+    torch = _torch()
+    if not items:
+        return [], [], [], None
+    device = items[0][0].device
+    _require_gpu(items[0][0])
+    p = params(group, n_clusters, iters, seed, variant)
+    n = len(items)
+    outputs = [_alloc_outputs(w.shape[0], w.shape[1], group, n_clusters, device, True) for w, _ in items]
+    cfs = [torch.empty((w.shape[0], n_clusters), dtype=torch.float32, device=device) for w, _ in items]
+    pks = [torch.empty((w.shape[0], n_clusters), dtype=torch.int32, device=device) for w, _ in items]
+    mats = (Any4Matrix * n)()
+    for i, (w, act) in enumerate(items):
+        mats[i] = _matrix(w, act, outputs[i], matrix_index=(matrix_indices[i] if matrix_indices else i),
+                          group=group, n_clusters=n_clusters)
+    cptr = (ctypes.c_void_p * n)(*[_ptr(c) for c in cfs])
+    pptr = (ctypes.c_void_p * n)(*[_ptr(q) for q in pks])
+    ws = workspace(device, workspace_bytes(mats, n, p))
+    _check(lib().any4_stage_quantize_batch(mats, n, ctypes.byref(p), cptr, pptr, _ptr(ws), ws.numel(),
+                                           _stream(device)), "any4_stage_quantize_batch")
+    return outputs, cfs, pks, ws

@@ -142,6 +142,121 @@ int validate_batch(const any4_matrix* mats, int32_t count, const any4_params* p)
   return ANY4_OK;
 }
 
+
+// The batched path: every matrix of the batch through the row kernel, matrices of one
+// row geometry in one launch (up to kMaxMats each), longer rows first so that the
+// longest blocks start earliest.  Restart r (Philox counters t + 16 r): the first writes
+// the outputs, each later one writes candidates into the workspace that replace a row's
+// outputs where its objective is lower.  c_final / picks: optional per-matrix device
+// arrays (or NULL) for the fp32 centroids and the k-means++ picks of the kept run.
+// `order` and `rb` are caller storage for `count` entries; arguments are validated and
+// the workspace is at least workspace_bytes_for() large.
+int quantize_core(const any4_matrix* mats, int32_t count, const any4_params* params,
+                  float* const* c_final, int32_t* const* picks, unsigned char* workspace,
+                  hipStream_t stream, int32_t* order, RestartBufs* rb) {
+  uint32_t* status = reinterpret_cast<uint32_t*>(workspace);
+  if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
+  const int R = restarts_of(params);
+  const int k = params->n_clusters;
+  if (R > 1) {
+    unsigned char* base = workspace + kWorkspaceBytes;
+    for (int32_t i = 0; i < count; ++i) rb[i] = carve_restart(base, &mats[i], k);
+  }
+  int32_t n_order = 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (mats[i].n_rows > 0) order[n_order++] = i;
+  std::stable_sort(order, order + n_order, [&](int32_t x, int32_t y) {
+    return mats[x].n_cols > mats[y].n_cols;
+  });
+  auto cf = [&](int32_t i) { return c_final ? c_final[i] : nullptr; };
+  auto pk = [&](int32_t i) { return picks ? picks[i] : nullptr; };
+  for (int r = 0; r < R; ++r) {
+    int32_t i = 0;
+    while (i < n_order) {
+      const RowConfig cfg = any4::choose_config(mats[order[i]].n_cols);
+      LaunchArgs a = make_args(params, cfg.nw, status);
+      a.restart = r;
+      int64_t rows = 0;
+      a.n_mats = 0;
+      while (i < n_order && a.n_mats < any4::kMaxMats) {
+        const RowConfig c2 = any4::choose_config(mats[order[i]].n_cols);
+        if (c2.e != cfg.e || c2.nw != cfg.nw) break;
+        if (rows + mats[order[i]].n_rows > INT32_MAX) break;
+        const int32_t mi = order[i];
+        const any4_matrix* m = &mats[mi];
+        MatDesc d = make_desc(m);
+        d.c_out = cf(mi);
+        d.picks_out = pk(mi);
+        if (R > 1) {
+          const RestartBufs& b = rb[mi];
+          double* best = m->objective ? m->objective : b.best_obj;
+          if (r == 0) {
+            d.objective = best;
+          } else {
+            d.codes = b.codes;
+            d.lut = b.lut;
+            d.objective = b.obj;
+            d.c_out = cf(mi) ? b.c : nullptr;
+            d.picks_out = pk(mi) ? b.picks : nullptr;
+          }
+        }
+        a.row_start[a.n_mats] = rows;
+        a.m[a.n_mats] = d;
+        rows += m->n_rows;
+        ++a.n_mats;
+        ++i;
+      }
+      for (int j = a.n_mats; j <= any4::kMaxMats; ++j) a.row_start[j] = rows;
+      if (any4::launch_rows(a, cfg, any4::MODE_FULL, rows, stream) != hipSuccess)
+        return ANY4_ERR_HIP;
+    }
+    if (r == 0) continue;
+    for (int32_t oi = 0; oi < n_order; ++oi) {
+      const int32_t mi = order[oi];
+      const any4_matrix* m = &mats[mi];
+      const RestartBufs& b = rb[mi];
+      any4::MergeDesc md;
+      std::memset(&md, 0, sizeof(md));
+      md.n_rows = m->n_rows;
+      md.n_cols = m->n_cols;
+      md.n_clusters = k;
+      md.cand_codes = b.codes;
+      md.cand_lut = b.lut;
+      md.cand_obj = b.obj;
+      md.cand_c = cf(mi) ? b.c : nullptr;
+      md.cand_picks = pk(mi) ? b.picks : nullptr;
+      md.codes = m->codes;
+      md.lut = m->lut;
+      md.best_obj = m->objective ? m->objective : b.best_obj;
+      md.c = cf(mi);
+      md.picks = pk(mi);
+      if (any4::launch_restart_merge(md, stream) != hipSuccess) return ANY4_ERR_HIP;
+    }
+  }
+  return ANY4_OK;
+}
+
+size_t workspace_bytes_for(const any4_matrix* mats, int32_t count, const any4_params* params) {
+  size_t bytes = kWorkspaceBytes;
+  if (restarts_of(params) > 1)
+    for (int32_t i = 0; i < count; ++i) bytes += restart_bytes(&mats[i], params->n_clusters);
+  return bytes;
+}
+
+// Validation, workspace check and host storage for the batched path.
+int quantize_checked(const any4_matrix* mats, int32_t count, const any4_params* params,
+                     float* const* c_final, int32_t* const* picks, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_batch(mats, count, params);
+  if (st != ANY4_OK) return st;
+  if (!workspace || workspace_bytes < workspace_bytes_for(mats, count, params))
+    return ANY4_ERR_WORKSPACE;
+  std::vector<int32_t> order(static_cast<size_t>(count));
+  std::vector<RestartBufs> rb(static_cast<size_t>(count));
+  return quantize_core(mats, count, params, c_final, picks, static_cast<unsigned char*>(workspace),
+                       stream, order.data(), rb.data());
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,94 +287,19 @@ int any4_workspace_bytes(const any4_matrix* mats, int32_t count, const any4_para
   if (!bytes_out) return ANY4_ERR_INVALID_ARG;
   const int st = validate_batch(mats, count, params);
   if (st != ANY4_OK) return st;
-  size_t bytes = kWorkspaceBytes;
-  if (restarts_of(params) > 1)
-    for (int32_t i = 0; i < count; ++i) bytes += restart_bytes(&mats[i], params->n_clusters);
-  *bytes_out = bytes;
+  *bytes_out = workspace_bytes_for(mats, count, params);
   return ANY4_OK;
 }
 
 int any4_quantize(const any4_matrix* mats, int32_t count, const any4_params* params,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = validate_batch(mats, count, params);
-  if (st != ANY4_OK) return st;
-  size_t need = 0;
-  any4_workspace_bytes(mats, count, params, &need);
-  if (!workspace || workspace_bytes < need) return ANY4_ERR_WORKSPACE;
-  uint32_t* status = static_cast<uint32_t*>(workspace);
-  if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
-  const int R = restarts_of(params);
-  const int k = params->n_clusters;
-  std::vector<RestartBufs> rb(static_cast<size_t>(count));
-  if (R > 1) {
-    unsigned char* base = static_cast<unsigned char*>(workspace) + kWorkspaceBytes;
-    for (int32_t i = 0; i < count; ++i) rb[i] = carve_restart(base, &mats[i], k);
-  }
+  return quantize_checked(mats, count, params, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
 
-  // Matrices sharing a row geometry go into one launch (up to kMaxMats each);
-  // longer rows first so that the longest blocks start earliest.
-  std::vector<int32_t> order;
-  for (int32_t i = 0; i < count; ++i)
-    if (mats[i].n_rows > 0) order.push_back(i);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    return mats[x].n_cols > mats[y].n_cols;
-  });
-  // Restart r (Philox counters t + 16 r): the first writes the outputs, each later one
-  // writes candidates that replace a row's outputs where its objective is lower.
-  for (int r = 0; r < R; ++r) {
-    size_t i = 0;
-    while (i < order.size()) {
-      const RowConfig cfg = any4::choose_config(mats[order[i]].n_cols);
-      LaunchArgs a = make_args(params, cfg.nw, status);
-      a.restart = r;
-      int64_t rows = 0;
-      a.n_mats = 0;
-      while (i < order.size() && a.n_mats < any4::kMaxMats) {
-        const RowConfig c2 = any4::choose_config(mats[order[i]].n_cols);
-        if (c2.e != cfg.e || c2.nw != cfg.nw) break;
-        if (rows + mats[order[i]].n_rows > INT32_MAX) break;
-        const any4_matrix* m = &mats[order[i]];
-        MatDesc d = make_desc(m);
-        if (R > 1) {
-          const RestartBufs& b = rb[order[i]];
-          double* best = m->objective ? m->objective : b.best_obj;
-          if (r == 0) {
-            d.objective = best;
-          } else {
-            d.codes = b.codes;
-            d.lut = b.lut;
-            d.objective = b.obj;
-          }
-        }
-        a.row_start[a.n_mats] = rows;
-        a.m[a.n_mats] = d;
-        rows += m->n_rows;
-        ++a.n_mats;
-        ++i;
-      }
-      for (int j = a.n_mats; j <= any4::kMaxMats; ++j) a.row_start[j] = rows;
-      if (any4::launch_rows(a, cfg, any4::MODE_FULL, rows, stream) != hipSuccess)
-        return ANY4_ERR_HIP;
-    }
-    if (r == 0) continue;
-    for (int32_t idx : order) {
-      const any4_matrix* m = &mats[idx];
-      const RestartBufs& b = rb[idx];
-      any4::MergeDesc md;
-      std::memset(&md, 0, sizeof(md));
-      md.n_rows = m->n_rows;
-      md.n_cols = m->n_cols;
-      md.n_clusters = k;
-      md.cand_codes = b.codes;
-      md.cand_lut = b.lut;
-      md.cand_obj = b.obj;
-      md.codes = m->codes;
-      md.lut = m->lut;
-      md.best_obj = m->objective ? m->objective : b.best_obj;
-      if (any4::launch_restart_merge(md, stream) != hipSuccess) return ANY4_ERR_HIP;
-    }
-  }
-  return ANY4_OK;
+int any4_stage_quantize_batch(const any4_matrix* mats, int32_t count, const any4_params* params,
+                              float* const* c_final, int32_t* const* picks, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return quantize_checked(mats, count, params, c_final, picks, workspace, workspace_bytes, stream);
 }
 
 int any4_read_device_status(const void* workspace, hipStream_t stream) {
@@ -349,58 +389,7 @@ int any4_stage_pack(const any4_matrix* m, const any4_params* params, const uint8
 
 int any4_stage_full(const any4_matrix* m, const any4_params* params, float* c_final,
                     int32_t* picks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = validate_batch(m, 1, params);
-  if (st != ANY4_OK) return st;
-  size_t need = 0;
-  any4_workspace_bytes(m, 1, params, &need);
-  if (!workspace || workspace_bytes < need) return ANY4_ERR_WORKSPACE;
-  uint32_t* status = static_cast<uint32_t*>(workspace);
-  if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
-  const int R = restarts_of(params);
-  RestartBufs b{};
-  if (R > 1) {
-    unsigned char* base = static_cast<unsigned char*>(workspace) + kWorkspaceBytes;
-    b = carve_restart(base, m, params->n_clusters);
-  }
-  double* best = m->objective ? m->objective : b.best_obj;
-  for (int r = 0; r < R; ++r) {
-    MatDesc d = make_desc(m);
-    d.c_out = c_final;
-    d.picks_out = picks;
-    if (R > 1) {
-      if (r == 0) {
-        d.objective = best;
-      } else {
-        d.codes = b.codes;
-        d.lut = b.lut;
-        d.objective = b.obj;
-        d.c_out = c_final ? b.c : nullptr;
-        d.picks_out = picks ? b.picks : nullptr;
-      }
-    }
-    LaunchArgs a = make_args(params, 1, status);
-    a.restart = r;
-    st = launch_one(a, d, any4::MODE_FULL, stream);
-    if (st != ANY4_OK) return st;
-    if (r == 0 || m->n_rows == 0) continue;
-    any4::MergeDesc md;
-    std::memset(&md, 0, sizeof(md));
-    md.n_rows = m->n_rows;
-    md.n_cols = m->n_cols;
-    md.n_clusters = params->n_clusters;
-    md.cand_codes = b.codes;
-    md.cand_lut = b.lut;
-    md.cand_obj = b.obj;
-    md.cand_c = c_final ? b.c : nullptr;
-    md.cand_picks = picks ? b.picks : nullptr;
-    md.codes = m->codes;
-    md.lut = m->lut;
-    md.best_obj = best;
-    md.c = c_final;
-    md.picks = picks;
-    if (any4::launch_restart_merge(md, stream) != hipSuccess) return ANY4_ERR_HIP;
-  }
-  return ANY4_OK;
+  return quantize_checked(m, 1, params, &c_final, &picks, workspace, workspace_bytes, stream);
 }
 
 int any4_act_absmean_workspace_bytes(int64_t n_tokens, int64_t n_cols, size_t* bytes_out) {

@@ -1171,6 +1171,8 @@ void any4_rows_kernel(const LaunchArgs args) {
       else
         element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
     }
+    // the reduction reads bins that other lanes of this wave just added to
+    wave_lds_fence();
     const double total = reduce_bins(bins, lane);
     if ((lane & 1) == 0) S.wred[wave][lane >> 1] = total - prev_total;
     prev_total = total;
