@@ -208,6 +208,24 @@ int any4_stage_quantize_batch(const any4_matrix* mats, int32_t count, const any4
                               float* const* c_final, int32_t* const* picks, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): any4_quantize without a workspace.
+ * The status word and, with restarts, the candidate outputs live in a library-owned
+ * device array of ANY4_NOALLOC_SCRATCH_BYTES on each device (a static device array,
+ * held until the process ends); the call allocates nothing.  The batch may hold at
+ * most ANY4_NOALLOC_MAX_MATRICES matrices (else ANY4_ERR_UNSUPPORTED) and need at most
+ * ANY4_NOALLOC_SCRATCH_BYTES of workspace as any4_workspace_bytes counts it (else
+ * ANY4_ERR_WORKSPACE), both checked before any launch; without restarts every batch
+ * fits.  status_out: optional device pointer that receives, in stream order, this
+ * call's status word (ANY4_OK or ANY4_ERR_NONFINITE).  The array keeps the last call's
+ * contents, and this call clears what it reads; calls that overlap on one GPU (other
+ * streams or threads) share it and race, so serialize them.  Otherwise the same as
+ * any4_quantize, with the same outputs bit for bit. */
+#define ANY4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define ANY4_NOALLOC_MAX_MATRICES 64
+int any4_quantize_noalloc(const any4_matrix* mats, int32_t count, const any4_params* params,
+                          uint32_t* status_out, hipStream_t stream);
+
 /* ---- bookends: the calibration statistic the quantizer consumes and the
  * dequantization of what it emits. ---- */
 

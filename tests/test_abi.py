@@ -129,6 +129,27 @@ def test_quantize_rejects_before_launch(L):
     assert L.any4_stage_full(ctypes.byref(m), ctypes.byref(p), None, None, None, 0, None) == 3
 
 
+def test_noalloc_validates_before_launch(L):
+    """The entry point that allocates nothing refuses bad batches, too many matrices and
+    batches that need more than its scratch, all before any HIP call."""
+    p = any4.params(128, 16, 20, 0)
+    m = _mat()
+    assert L.any4_quantize_noalloc(None, 1, ctypes.byref(p), None, None) == 1
+    assert L.any4_quantize_noalloc(ctypes.byref(m), 1, ctypes.byref(any4.params(100)), None, None) == 1
+    assert L.any4_quantize_noalloc(ctypes.byref(_mat(k=65536)), 1, ctypes.byref(p), None, None) == 2
+    many = (any4.Any4Matrix * (any4.NOALLOC_MAX_MATRICES + 1))(*[_mat() for _ in range(any4.NOALLOC_MAX_MATRICES + 1)])
+    assert L.any4_quantize_noalloc(many, any4.NOALLOC_MAX_MATRICES + 1, ctypes.byref(p), None, None) == 2
+    # restarts on 20000 x 4096 need ~41 MB of candidates: more than the 32 MiB scratch
+    big = _mat(n=20000, k=4096)
+    pr = any4.params(128, 16, 20, 0, any4.RESTARTS(2))
+    st, need = _ws_bytes(L, big, pr)
+    assert st == 0 and need > any4.NOALLOC_SCRATCH_BYTES
+    assert L.any4_quantize_noalloc(ctypes.byref(big), 1, ctypes.byref(pr), None, None) == 3
+    # the headline matrix with restarts fits
+    st, need = _ws_bytes(L, _mat(n=14336, k=4096), pr)
+    assert st == 0 and need <= any4.NOALLOC_SCRATCH_BYTES
+
+
 def test_bookends_validate_before_launch(L):
     """E|x| and dequantization reject bad arguments synchronously (no HIP call)."""
     n = ctypes.c_size_t(0)

@@ -27,12 +27,15 @@ def RESTARTS(n: int) -> int:
 ANY4_OK = 0
 ANY4_ERR_NONFINITE = 5
 WORKSPACE_BYTES = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ANY4_NOALLOC_SCRATCH_BYTES
+NOALLOC_MAX_MATRICES = 64          # ANY4_NOALLOC_MAX_MATRICES
 
 EXPORTED = [
     "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
     "any4_stage_full", "any4_stage_lloyd_sorted", "any4_stage_quantize_batch",
+    "any4_quantize_noalloc",
     "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize", "any4_lut_gemv",
 ]
 
@@ -83,6 +86,7 @@ def lib():
         P, MP, PP = ctypes.c_void_p, ctypes.POINTER(Any4Matrix), ctypes.POINTER(Any4Params)
         L.any4_workspace_bytes.argtypes = [MP, ctypes.c_int32, PP, ctypes.POINTER(ctypes.c_size_t)]
         L.any4_quantize.argtypes = [MP, ctypes.c_int32, PP, P, ctypes.c_size_t, P]
+        L.any4_quantize_noalloc.argtypes = [MP, ctypes.c_int32, PP, P, P]
         L.any4_read_device_status.argtypes = [P, P]
         L.any4_status_string.argtypes = [ctypes.c_int]
         L.any4_status_string.restype = ctypes.c_char_p
@@ -280,6 +284,31 @@ def quantize(w, act, group: int = 128, n_clusters: int = 16, iters: int = 20, se
     _check(lib().any4_quantize(ctypes.byref(m), 1, ctypes.byref(p), _ptr(ws), ws.numel(),
                                _stream(w.device)), "any4_quantize")
     return out
+
+
+def quantize_noalloc(items: Sequence[Tuple[object, object]], outputs: List[Quantized], group: int = 128,
+                     n_clusters: int = 16, iters: int = 20, seed: int = 0, status_out=None,
+                     matrix_indices: Optional[Sequence[int]] = None, variant: int = 0) -> List[Quantized]:
+    """any4_quantize_noalloc: the batched quantizer with no workspace and no device
+    allocation in the library (its scratch is a library-owned device array).  The caller
+    passes preallocated outputs; status_out is an optional int32 [1] device tensor that
+    receives the status word.  Calls that overlap on one GPU race on the scratch."""
+    if not items:
+        return []
+    device = items[0][0].device
+    _require_gpu(items[0][0])
+    p = params(group, n_clusters, iters, seed, variant)
+    mats = (Any4Matrix * len(items))()
+    for i, (w, act) in enumerate(items):
+        mats[i] = _matrix(w, act, outputs[i], matrix_index=(matrix_indices[i] if matrix_indices else i),
+                          group=group, n_clusters=n_clusters)
+    if status_out is not None:
+        torch = _torch()
+        if status_out.dtype != torch.int32 or status_out.numel() < 1 or status_out.device != device:
+            raise ValueError("status_out must be an int32 tensor on W's device")
+    _check(lib().any4_quantize_noalloc(mats, len(items), ctypes.byref(p), _ptr(status_out),
+                                       _stream(device)), "any4_quantize_noalloc")
+    return outputs
 
 
 def read_status(ws) -> int:

@@ -150,10 +150,11 @@ int validate_batch(const any4_matrix* mats, int32_t count, const any4_params* p)
 // outputs where its objective is lower.  c_final / picks: optional per-matrix device
 // arrays (or NULL) for the fp32 centroids and the k-means++ picks of the kept run.
 // `order` and `rb` are caller storage for `count` entries; arguments are validated and
-// the workspace is at least workspace_bytes_for() large.
+// the workspace is at least workspace_bytes_for() large.  in_place_sort orders the
+// matrices without heap memory (for the entry point that allocates nothing).
 int quantize_core(const any4_matrix* mats, int32_t count, const any4_params* params,
                   float* const* c_final, int32_t* const* picks, unsigned char* workspace,
-                  hipStream_t stream, int32_t* order, RestartBufs* rb) {
+                  hipStream_t stream, int32_t* order, RestartBufs* rb, bool in_place_sort) {
   uint32_t* status = reinterpret_cast<uint32_t*>(workspace);
   if (any4::launch_clear_status(status, stream) != hipSuccess) return ANY4_ERR_HIP;
   const int R = restarts_of(params);
@@ -165,9 +166,19 @@ int quantize_core(const any4_matrix* mats, int32_t count, const any4_params* par
   int32_t n_order = 0;
   for (int32_t i = 0; i < count; ++i)
     if (mats[i].n_rows > 0) order[n_order++] = i;
-  std::stable_sort(order, order + n_order, [&](int32_t x, int32_t y) {
-    return mats[x].n_cols > mats[y].n_cols;
-  });
+  if (!in_place_sort) {
+    std::stable_sort(order, order + n_order, [&](int32_t x, int32_t y) {
+      return mats[x].n_cols > mats[y].n_cols;
+    });
+  } else {
+    // the same stable order by insertion, which takes no heap memory
+    for (int32_t a = 1; a < n_order; ++a) {
+      const int32_t v = order[a];
+      int32_t b = a;
+      for (; b > 0 && mats[order[b - 1]].n_cols < mats[v].n_cols; --b) order[b] = order[b - 1];
+      order[b] = v;
+    }
+  }
   auto cf = [&](int32_t i) { return c_final ? c_final[i] : nullptr; };
   auto pk = [&](int32_t i) { return picks ? picks[i] : nullptr; };
   for (int r = 0; r < R; ++r) {
@@ -254,7 +265,7 @@ int quantize_checked(const any4_matrix* mats, int32_t count, const any4_params* 
   std::vector<int32_t> order(static_cast<size_t>(count));
   std::vector<RestartBufs> rb(static_cast<size_t>(count));
   return quantize_core(mats, count, params, c_final, picks, static_cast<unsigned char*>(workspace),
-                       stream, order.data(), rb.data());
+                       stream, order.data(), rb.data(), false);
 }
 
 }  // namespace
@@ -300,6 +311,25 @@ int any4_stage_quantize_batch(const any4_matrix* mats, int32_t count, const any4
                               float* const* c_final, int32_t* const* picks, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
   return quantize_checked(mats, count, params, c_final, picks, workspace, workspace_bytes, stream);
+}
+
+int any4_quantize_noalloc(const any4_matrix* mats, int32_t count, const any4_params* params,
+                          uint32_t* status_out, hipStream_t stream) {
+  const int st = validate_batch(mats, count, params);
+  if (st != ANY4_OK) return st;
+  if (count > ANY4_NOALLOC_MAX_MATRICES) return ANY4_ERR_UNSUPPORTED;
+  static_assert(ANY4_NOALLOC_SCRATCH_BYTES == any4::kNoallocScratchBytes, "scratch size");
+  if (workspace_bytes_for(mats, count, params) > any4::kNoallocScratchBytes) return ANY4_ERR_WORKSPACE;
+  unsigned char* scratch = nullptr;
+  if (any4::noalloc_scratch(&scratch) != hipSuccess) return ANY4_ERR_HIP;
+  int32_t order[ANY4_NOALLOC_MAX_MATRICES];
+  RestartBufs rb[ANY4_NOALLOC_MAX_MATRICES];
+  const int r = quantize_core(mats, count, params, nullptr, nullptr, scratch, stream, order, rb, true);
+  if (r != ANY4_OK) return r;
+  if (status_out &&
+      any4::launch_copy_status(reinterpret_cast<const uint32_t*>(scratch), status_out, stream) != hipSuccess)
+    return ANY4_ERR_HIP;
+  return ANY4_OK;
 }
 
 int any4_read_device_status(const void* workspace, hipStream_t stream) {

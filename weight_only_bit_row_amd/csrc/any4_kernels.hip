@@ -4,12 +4,25 @@
 // The row kernel itself is in any4_rows.h, instantiated by any4_rows_e*.hip.
 #include "any4_rows.h"
 
+#include <mutex>
+
 namespace any4 {
 namespace {
 
 __global__ void clear_status_kernel(uint32_t* status) {
   if (threadIdx.x == 0) *status = 0u;
 }
+
+__global__ void copy_status_kernel(const uint32_t* src, uint32_t* dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
+// Scratch of the entry point that allocates nothing (any4_quantize_noalloc): the status
+// word and, with restarts, the candidate outputs.  Every device that runs the library
+// holds its own copy until the process ends.  Host code must never pass `scratch` itself
+// to a kernel (on the host it names a stand-in, not the device array): it uses the
+// per-device address from noalloc_scratch() below.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 // Emission only, from given assignments/centroids/scales: one thread per packed byte.
 __global__ void pack_kernel(MatDesc M, int group, int k, const uint8_t* assign, const float* c,
@@ -321,6 +334,34 @@ hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
   d.kp = kp;
   hipLaunchKernelGGL(sorted_lloyd_kernel, dim3(static_cast<unsigned>(d.n_rows)), dim3(kSortedThreads),
                      sorted_lloyd_lds_bytes(d.n_cols), stream, d);
+  return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per device (under a
+// lock, so concurrent first calls are safe) and kept.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_lock;
+unsigned char* g_scratch[kMaxScratchDevices];
+
+hipError_t noalloc_scratch(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(g_scratch_lock);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_copy_status(const uint32_t* src, uint32_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream, src, dst);
   return hipGetLastError();
 }
 

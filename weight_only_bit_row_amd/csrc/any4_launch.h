@@ -80,6 +80,13 @@ hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t 
                        hipStream_t stream);
 // Clear the status word (a one-thread kernel: no memset node is recorded).
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
+// Copy the status word to a caller's buffer (a one-thread kernel).
+hipError_t launch_copy_status(const uint32_t* src, uint32_t* dst, hipStream_t stream);
+
+// Library-owned scratch of any4_quantize_noalloc: kNoallocScratchBytes of device memory per
+// device (a static device array), its address on the current device looked up on first use.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(unsigned char** out);
 // Emission-only kernel behind any4_stage_pack.
 hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_t* assign,
                        const float* c, const float* alpha, const float* beta, hipStream_t stream);
