@@ -12,10 +12,17 @@ outputs are preallocated.  Prints ONE JSON line.
   python bench.py --bookends-only --profile-steps 5   # only E|x| and dequantization
   python bench.py --sorted-only --profile-steps 5     # only the sorted-row Lloyd stage
 
-The same line reports the two bookend kernels (E|x| of a calibration batch and the
-Eq. 4 dequantization of the quantized matrix) against the HBM roofline under
-"bookends", and the sorted-row Lloyd stage on the same matrix under "sorted_lloyd";
-they run after the timed quantizer steps and are not part of `value`.
+Beside `value` (after the timed quantizer steps, not part of it) the same line reports:
+  configs       every other named workload (toy, q_proj at g=128 and 64, the Llama3-70B
+                down_proj, the one-call Llama3-8B layer as any4/any3/any2): ms per call,
+                Lloyd elem-iters/s from t(20 rounds) - t(0) and the credited FP32 share;
+  bookends      E|x| of a calibration batch, the Eq. 4 dequantization and the LUT
+                matrix-vector products against the HBM roofline;
+  sorted_lloyd  the sorted-row Lloyd stage on the headline matrix;
+  cpu_baseline  the oracle on the host, on one pinned core and on all usable cores (at
+                most 16), for every workload, measured before the GPU is touched.
+
+  python bench.py --profile-steps 30 --workload down_70b   # another workload under a profiler
 """
 from __future__ import annotations
 
@@ -65,39 +72,84 @@ def load_traffic(counters: str = COUNTERS, src: str = KERNEL_SRC, key: str = "tr
     return float(t.group(1))
 
 
-def cpu_baseline(m, group, k, iters, n_rows_sample=14336):
-    """The CPU oracle, as it is, on a bounded row sample of the same matrix, spread over
-    the host's cores with threads (ctypes releases the GIL)."""
-    from concurrent.futures import ThreadPoolExecutor
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    import numpy as np
+
+def _shards(mats, n_shards, max_rows):
+    """Contiguous row shards of about equal element count over the first rows of every
+    matrix (the same fraction of each, a row sample when the workload has more than
+    max_rows rows).  Returns ([[(Matrix, lo, hi), ...] per shard], rows used, rows)."""
+    total_rows = sum(m.w.shape[0] for m in mats)
+    frac = min(1.0, max_rows / total_rows)
+    rows = [(m, r) for m in mats for r in range(max(1, int(round(m.w.shape[0] * frac))))]
+    elems = sum(m.w.shape[1] for m, _ in rows)
+    shards = [[] for _ in range(n_shards)]
+    acc = 0
+    for m, r in rows:
+        si = min(n_shards - 1, int(acc * n_shards / elems))
+        acc += m.w.shape[1]
+        sh = shards[si]
+        if sh and sh[-1][0] is m and sh[-1][2] == r:
+            sh[-1] = (m, sh[-1][1], r + 1)
+        else:
+            sh.append((m, r, r + 1))
+    return [sh for sh in shards if sh], len(rows), total_rows
+
+
+def _run_shards(shards, group, k, iters):
+    """The oracle (plain single-threaded C; ctypes releases the GIL) on each shard, one
+    thread per shard, each thread pinned to its own core with sched_setaffinity (what
+    taskset does).  Returns (wall seconds, elem-iters done)."""
+    import threading
 
     import oracle
 
-    cores = min(16, len(os.sched_getaffinity(0)))
-    rows = min(n_rows_sample, m.w.shape[0])
-    bounds = np.linspace(0, rows, cores + 1).astype(int)
-
-    def work(c):
-        lo, hi = bounds[c], bounds[c + 1]
-        if hi > lo:
-            oracle.quantize(m.w[lo:hi], m.dtype, m.act, group, k, iters, seed=0, row_offset=int(lo))
-
     oracle.lib()
+    cpus = sorted(os.sched_getaffinity(0))
+    barrier = threading.Barrier(len(shards) + 1)
+    work = sum((hi - lo) * m.w.shape[1] * iters for sh in shards for m, lo, hi in sh)
+
+    def run(pieces, cpu):
+        os.sched_setaffinity(0, {cpu})      # this thread only
+        barrier.wait()
+        for m, lo, hi in pieces:
+            oracle.quantize(m.w[lo:hi], m.dtype, m.act, group, k, iters, seed=0, row_offset=int(lo),
+                            matrix_index=m.matrix_index)
+
+    threads = [threading.Thread(target=run, args=(sh, cpus[i % len(cpus)])) for i, sh in enumerate(shards)]
+    for t in threads:
+        t.start()
+    barrier.wait()
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(cores) as ex:
-        list(ex.map(work, range(cores)))
-    dt = time.perf_counter() - t0
-    K = m.w.shape[1]
-    return {
-        "value": rows * K * iters / dt,
-        "unit": "elem-iters/s",
-        "cores": cores,
-        "kind": "oracle",
-        "sample": f"first {rows} of {m.w.shape[0]} rows of the same matrix, full path "
-                  f"(scale, k-means++, {iters} Lloyd rounds, final E-step, emission); "
-                  f"{dt:.2f} s wall on {cores} threads",
-    }
+    for t in threads:
+        t.join()
+    return time.perf_counter() - t0, work
+
+
+def cpu_baseline_config(mats, group, k, iters, cores, one_core_budget=4e7, per_core_budget=8e7):
+    """The oracle, as it is, on a bounded row sample of a workload (about `budget`
+    elem-iters): on one pinned core, and on `cores` pinned cores with one contiguous row
+    shard each.  Throughput is the sample's elem-iters over its wall time; ms per call
+    extrapolates that throughput linearly to the whole workload."""
+    K_avg = sum(m.w.size for m in mats) / sum(m.w.shape[0] for m in mats)
+    full_work = sum(m.w.size for m in mats) * iters
+
+    def run(n_cores, budget):
+        shards, used, total = _shards(mats, n_cores, max(n_cores, int(budget / (K_avg * max(iters, 1)))))
+        dt, work = _run_shards(shards, group, k, iters)
+        rate = work / dt
+        return {"cores": len(shards), "rows": used, "of_rows": total, "wall_s": dt,
+                "elem_iters_per_s": rate, "ms_per_call": full_work / rate * 1e3,
+                "extrapolated": used < total}
+
+    return run(1, one_core_budget), run(cores, per_core_budget * cores)
 
 
 def copy_calibration():
@@ -255,6 +307,83 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
     ]
 
 
+CONFIG_NAMES = ["tiny", "q_proj_g128", "q_proj_g64", "down_70b", "layer_any4", "layer_any3",
+                "layer_any2"]
+
+
+def load_workloads(names):
+    """The named workloads, generated once (q_proj at g=64 and g=128 share their matrix,
+    the layer's three bit widths share its seven matrices)."""
+    from workloads import Workload, make
+
+    out, cache = {}, {}
+    for n in names:
+        if n.startswith("q_proj"):
+            base = cache.setdefault("q_proj", make("q_proj_g128"))
+            out[n] = Workload(n, base.matrices, 128 if n.endswith("128") else 64, 16, 20)
+        elif n.startswith("layer_any"):
+            base = cache.setdefault("layer", make("layer_any4"))
+            out[n] = Workload(n, base.matrices, 128, 1 << int(n[-1]), 20)
+        else:
+            out[n] = make(n)
+    return out
+
+
+def describe(wl) -> str:
+    shapes = " + ".join(f"{m.w.shape[0]}x{m.w.shape[1]}" for m in wl.matrices)
+    return (f"{wl.name}: {shapes} {'bf16' if wl.matrices[0].dtype == 1 else 'fp32'}, group {wl.group}, "
+            f"{wl.n_clusters} clusters, {wl.iters} Lloyd rounds, Philox seed 0")
+
+
+def gpu_config(any4, torch, wl, dev, stream, steps=10, warmup=2):
+    """One named workload in one call (a batch for the layer): median HIP-event time of
+    the whole call at the workload's rounds and at 0 rounds; the Lloyd rate credits
+    3k+1 flops per element-round over the difference."""
+    import numpy as np
+
+    items = []
+    for m in wl.matrices:
+        if m.dtype == 1:
+            w = torch.from_numpy(m.w.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            w = torch.from_numpy(m.w).to(dev)
+        items.append((w, torch.from_numpy(m.act).to(dev)))
+    idx = [m.matrix_index for m in wl.matrices]
+    g, k, iters = wl.group, wl.n_clusters, wl.iters
+    outs = any4.quantize_batch(items, group=g, n_clusters=k, iters=iters, matrix_indices=idx)
+    ws = any4.workspace(dev)
+
+    def med(n_iters, n):
+        for _ in range(warmup):
+            any4.quantize_batch(items, group=g, n_clusters=k, iters=n_iters, outputs=outs, ws=ws,
+                                matrix_indices=idx)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            any4.quantize_batch(items, group=g, n_clusters=k, iters=n_iters, outputs=outs, ws=ws,
+                                matrix_indices=idx)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    t = med(iters, steps)
+    t0 = med(0, steps)
+    status = any4.read_status(ws)
+    elems = wl.elements
+    lloyd = t - t0
+    res = {"workload": describe(wl), "elements": elems, "rows": wl.rows, "device_status": status,
+           "ms_per_call": t, "ms_iters0": t0, "lloyd_ms": lloyd,
+           "elem_iters_per_s": elems * iters / (t * 1e-3),
+           "lloyd_elem_iters_per_s": elems * iters / (lloyd * 1e-3) if lloyd > 0 else None,
+           "lloyd_pct_fp32_peak_credited": (elems * iters * (3 * k + 1) / (lloyd * 1e-3) / 1e12
+                                            / PEAK_FP32_TFLOPS * 100) if lloyd > 0 else None,
+           "whole_call_frac_credited": credited_flops_per_element(k, iters) * elems / (t * 1e-3) / 1e12
+                                       / PEAK_FP32_TFLOPS}
+    del items, outs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,10 +391,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many quantize calls (for rocprofv3), no baseline")
+    ap.add_argument("--workload", default="up_proj",
+                    help="with --profile-steps: the named workload to run (default up_proj)")
     ap.add_argument("--iters", type=int, default=None,
                     help="Lloyd rounds for --profile-steps runs (default: the workload's 20)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other named workloads (q_proj, 70B down_proj, layer)")
     ap.add_argument("--no-bookends", action="store_true",
                     help="skip the E|x|, dequant and LUT matrix-vector kernels")
     ap.add_argument("--sorted-only", action="store_true",
@@ -286,15 +419,66 @@ def main():
     import torch
 
     import weight_only_bit_row_amd as any4
-    from workloads import make
 
-    wl = make("up_proj")
+    profiling = bool(args.profile_steps) or args.sorted_only
+    head_name = args.workload if args.profile_steps else "up_proj"
+    names = [head_name]
+    if not profiling and not args.no_configs:
+        names += [n for n in CONFIG_NAMES if n != head_name]
+    wls = load_workloads(names)
+    wl = wls[head_name]
+
+    # The CPU oracle runs before anything touches the GPU: the headline matrix and every
+    # named workload, on one pinned core and on all usable cores (at most 16, the host
+    # share of one GPU), each on a bounded row sample.
+    cpu = None
+    if not profiling and not args.no_cpu_baseline:
+        avail = sorted(os.sched_getaffinity(0))
+        cores = min(16, len(avail))
+        per = {}
+        for n in names:
+            w_ = wls[n]
+            one, allc = cpu_baseline_config(w_.matrices, w_.group, w_.n_clusters, w_.iters, cores)
+            per[n] = {"workload": describe(w_), "one_core": one, "all_cores": allc}
+            print(f"cpu baseline {n}: 1 core {one['elem_iters_per_s']:.3g}, {allc['cores']} cores "
+                  f"{allc['elem_iters_per_s']:.3g} elem-iters/s", file=sys.stderr, flush=True)
+        head = per[head_name]["all_cores"]
+        cpu = {
+            "value": head["elem_iters_per_s"],
+            "unit": "elem-iters/s",
+            "cores": head["cores"],
+            "kind": "oracle",
+            "sample": (f"{head['rows']} of {head['of_rows']} rows of the same matrix, full path "
+                       f"(scale, k-means++, 20 Lloyd rounds, final E-step, emission), one thread per "
+                       f"contiguous row shard, each pinned to its own core; {head['wall_s']:.2f} s wall"),
+            "cpu_model": cpu_model(),
+            "nproc": os.cpu_count(),
+            "usable_cores": len(avail),
+            "single_core": per[head_name]["one_core"],
+            "per_config": [per[n] for n in names if n != head_name],
+        }
+
     m = wl.matrices[0]
     N, K = m.w.shape
     g, k, iters = wl.group, wl.n_clusters, wl.iters
     dev = torch.device("cuda:0")
-    w = torch.from_numpy(m.w.view(np.int16)).to(dev).view(torch.bfloat16)
+    if m.dtype == 1:
+        w = torch.from_numpy(m.w.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        w = torch.from_numpy(m.w).to(dev)
     act = torch.from_numpy(m.act).to(dev)
+    if args.profile_steps and len(wl.matrices) > 1:
+        items = [(torch.from_numpy(x.w.view(np.int16)).to(dev).view(torch.bfloat16),
+                  torch.from_numpy(x.act).to(dev)) for x in wl.matrices]
+        p_iters = iters if args.iters is None else args.iters
+        idx = [x.matrix_index for x in wl.matrices]
+        outs = any4.quantize_batch(items, group=g, n_clusters=k, iters=p_iters, matrix_indices=idx)
+        for _ in range(args.profile_steps):
+            any4.quantize_batch(items, group=g, n_clusters=k, iters=p_iters, outputs=outs,
+                                matrix_indices=idx)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": head_name}))
+        return
     out = any4.quantize(w, act, group=g, n_clusters=k, iters=iters)   # allocates outputs
     ws = any4.workspace(dev)
     torch.cuda.synchronize()
@@ -317,7 +501,8 @@ def main():
         for _ in range(args.profile_steps):
             any4.quantize(w, act, group=g, n_clusters=k, iters=p_iters, out=out, ws=ws)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.profile_steps, "status": any4.read_status(ws)}))
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": head_name,
+                          "status": any4.read_status(ws)}))
         return
 
     stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
@@ -384,12 +569,18 @@ def main():
             "kernel_ms_mean_hip_events": ms_kernel,
         },
     }
+    if not args.no_configs:
+        # every other named workload in one call each (not part of `value`)
+        line["configs"] = []
+        for n in names[1:]:
+            line["configs"].append(gpu_config(any4, torch, wls[n], dev, stream))
+            torch.cuda.synchronize()
     if not args.no_bookends:
         line["bookends"] = bookends(any4, torch, np, out, N, K, g, k, dev, stream)
         _, c_reg, _, _ = any4.stage_full(w, act, g, k, iters, seed=0)
         line["sorted_lloyd"] = sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, stream)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(m, g, k, iters)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line))
 
 
