@@ -282,18 +282,6 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
 
 }  // namespace
 
-// Launch geometry for a row length, from measurements: 32 elements per lane (several
-// waves per row) beat one 64-element wave per row on 14336 x 4096, whose register file
-// allows only one wave per SIMD.  Rows longer than 16384 keep 32 elements per lane on up
-// to 16 waves: against 64 elements on up to 8 waves (256 VGPRs, more spilled) they took
-// 7.7 ms instead of 8.3 on 8192 x 28672 and 3.0 instead of 3.9 on 4096 x 20480, with the
-// same output bits.
-RowConfig choose_config(int64_t K) {
-  if (K <= 512) return {8, 1};
-  if (K <= 1024) return {16, 1};
-  return {32, static_cast<int>((K + 2047) / 2048)};
-}
-
 hipError_t launch_rows(const LaunchArgs& args, RowConfig cfg, int mode, int64_t n_blocks,
                        hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;

@@ -66,7 +66,7 @@ struct RowConfig {
   int e;
   int nw;
 };
-RowConfig choose_config(int64_t n_cols);
+RowConfig choose_config(int64_t n_cols);  // any4_api.cpp
 
 // Row-kernel instances, one translation unit each (any4_rows_e*.hip): 8 or 16
 // elements per lane on one wave, 32 on one wave, 2-4 waves, and 5-16 waves.
