@@ -228,12 +228,18 @@ static float sqdist(float x, float c) {
  * every later one proportional to a_j * D_j, where D_j is the squared distance to
  * the nearest centre drawn so far.
  *
- * Sampling is done exactly in integers: with M = max_j p_j and e = floor(log2 M),
- * q_j = floor(p_j * 2^(40-e)) (so q_j < 2^41), Q = sum q_j, and one Philox4x32-10
- * draw per (row, t): u = x1 * 2^32 + x0 with counter (lo32(row), t, matrix,
- * hi32(row)) and key (lo32(seed), hi32(seed)); r = floor(u * Q / 2^64); the pick is
- * the smallest j whose prefix sum of q exceeds r.  When every p_j is 0 the centre
- * is copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1. */
+ * Sampling is done exactly in integers, with a fixed-point scale 2^(40-e):
+ * q_j = floor(p_j * 2^(40-e)), Q = sum q_j, and one Philox4x32-10 draw per (row, t):
+ * u = x1 * 2^32 + x0 with counter (lo32(row), t, matrix, hi32(row)) and key
+ * (lo32(seed), hi32(seed)); r = floor(u * Q / 2^64); the pick is the smallest j whose
+ * prefix sum of q exceeds r.  e = floor(log2 B) for a bound B on the draw's weights:
+ * B = max_j a_j for the first draw; for every later draw one bound, set after the first
+ * pick: B = fl(max_j a_j * fl(m * m)) with m = max(fl(x_max - c_0), fl(c_0 - x_min))
+ * over the row's scaled weights, which no later weight a_j * D_j exceeds (D_j only
+ * decreases, and rounding is monotone), so every q_j stays below 2^41.  (For the random
+ * initialization, whose weights are the a_j of the elements not yet drawn, B = max_j a_j
+ * throughout.)  When B = 0 or Q = 0 (every weight is 0, or below 2^(e-40)) the centre is
+ * copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1. */
 /* Initial centres for the initializations of Appendix C.2 (Table A4):
  *   init 0  k-means++ as described above;
  *   init 1  random: k distinct elements drawn one after another, each with probability
@@ -291,28 +297,42 @@ int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
     uint64_t* q = (uint64_t*)malloc((size_t)K * sizeof(uint64_t));
     if (!D || !p || !q) { free(D); free(p); free(q); return ORACLE_ERR_INVALID_ARG; }
 
+    /* bound of the first draw's weights, and the row's extremes for the later bound */
+    float a_max = 0.0f, x_min = ws[0], x_max = ws[0];
+    for (int64_t j = 0; j < K; ++j) {
+        if (a[j] > a_max) a_max = a[j];
+        if (ws[j] < x_min) x_min = ws[j];
+        if (ws[j] > x_max) x_max = ws[j];
+    }
+    float B = a_max;
     for (int32_t t = 0; t < k; ++t) {
-        float M = 0.0f;
         for (int64_t j = 0; j < K; ++j) {
             if (init == 1)
                 p[j] = (t == 0) ? a[j] : p[j];    /* drawn elements were set to 0 below */
             else
                 p[j] = (t == 0) ? a[j] : a[j] * D[j];
-            if (p[j] > M) M = p[j];
         }
-        if (M == 0.0f) {
-            c0[t] = (t == 0) ? ws[0] : c0[0];
-            picks[t] = -1;
-        } else {
+        if (t == 1 && init != 1) {
+            const float up = x_max - c0[0], down = c0[0] - x_min;
+            const float m = up > down ? up : down;
+            B = a_max * (m * m);
+        }
+        uint64_t Q = 0;
+        int e = 0;
+        if (B > 0.0f) {
             int E;
-            frexp((double)M, &E);               /* M = f * 2^E, f in [0.5, 1) */
-            int e = E - 1;                       /* floor(log2 M) */
-            uint64_t Q = 0;
+            frexp((double)B, &E);               /* B = f * 2^E, f in [0.5, 1) */
+            e = E - 1;                           /* floor(log2 B) */
             for (int64_t j = 0; j < K; ++j) {
                 double v = ldexp((double)p[j], 40 - e);
                 q[j] = (uint64_t)floor(v);
                 Q += q[j];
             }
+        }
+        if (Q == 0) {
+            c0[t] = (t == 0) ? ws[0] : c0[0];
+            picks[t] = -1;
+        } else {
             const uint32_t word1 = (uint32_t)(t + 16 * restart);
             uint64_t u = philox_u64(seed, row_id, word1, matrix_index);
             uint64_t r = (uint64_t)(((unsigned __int128)u * (unsigned __int128)Q) >> 64);

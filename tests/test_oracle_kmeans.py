@@ -301,6 +301,23 @@ def test_seed_picks_distinct_values_then_copies():
     assert np.all(c0 == x[0]) and np.all(picks == -1)
 
 
+def test_seed_scale_is_fixed_after_the_first_pick():
+    """After the first pick every draw uses one fixed-point scale 2^(40 - e), e from the
+    bound B = max a * m^2 (m the larger distance from the first centre to the row's
+    extremes).  Weights below 2^(e - 40) become 0: on a row whose other elements weigh
+    2^-60 against B = 225, the first centre is element 0 (the others' q_j are 0 even at
+    the first draw's scale 2^40), and every later draw has Q = 0, so it copies centre 0
+    (pick -1) although its weights are not all 0.  With weights 2^-20 instead (q_j =
+    floor(225 * 2^-20 * 2^33) > 0) the later draws do pick them."""
+    x = np.array([0.0, 15.0, 15.0, 15.0], np.float32)
+    for seed in range(20):
+        c0, picks = oracle.seed_row(x, np.array([1, 2 ** -60, 2 ** -60, 2 ** -60], np.float32), 4, seed=seed)
+        assert picks[0] == 0 and np.all(picks[1:] == -1) and np.all(c0 == 0.0), (seed, picks)
+        c0, picks = oracle.seed_row(x, np.array([1, 2 ** -20, 2 ** -20, 2 ** -20], np.float32), 4, seed=seed)
+        assert picks[0] == 0 and picks[1] in (1, 2, 3), (seed, picks)
+        assert np.all(picks[2:] == -1)        # after 15 is drawn every D is 0: copies
+
+
 def test_seed_depends_on_row_matrix_and_key():
     rng = np.random.default_rng(12)
     x = rng.uniform(0, 15, 256).astype(np.float32)
