@@ -107,6 +107,7 @@ struct Smem {
   int n_unique;
   int use_table;                        // this round's cell table is complete
   int bad[kMaxWaves];                           // per-wave vote: the row holds a bad value
+  float rstat[3][kMaxWaves];                    // per-wave max a, min w_S, max w_S
   int pad_[2];
 };
 
@@ -484,7 +485,7 @@ struct ScaleParams {
 // Eq. 1-2 (or Eq. 3) on one group held in registers [m0, m0+G), then the sample weights
 // of Eq. 23 (alpha * E|x|, or the ablated terms of Appendix C.1: E|x| alone, or 1).
 // Writes alpha/beta of the group (fp32 for the scale stage, fp16 otherwise).
-template <int MODE>
+template <int MODE, bool RECIP>
 __device__ __forceinline__ void finish_group(float mn, float mx, const ScaleParams& sp, float* x,
                                              float* act, int n, bool& bad, const MatDesc& M,
                                              int64_t row, int64_t gidx, int64_t n_groups,
@@ -495,12 +496,22 @@ __device__ __forceinline__ void finish_group(float mn, float mx, const ScalePara
   const float beta = sym ? 0.0f : mn;
   const int wmode = sp.variant & kVarWeightMask;
   if (!is_finite(alpha)) bad = true;
+  // w_S = fl32(diff / alpha) without a division per element: alpha is one value per
+  // group, so its reciprocal is taken once in fp64 and each quotient is
+  // fl32(fl64(diff * fl64(1 / alpha))).  The fp64 product lies within 2^-52 (relative)
+  // of the exact quotient, and a quotient of two fp32 values that is not itself an fp32
+  // value lies at least 2^-49 (relative) from every fp32 rounding midpoint, so rounding
+  // it to fp32 gives the correctly rounded quotient the division would.
+  // RECIP is set where a lane holds one group (groups at least as wide as a lane's
+  // columns); groups narrower than that keep one fp32 division per element, one in flight
+  // at a time, since several reciprocals held at once would cost registers.
+  const double rinv = (RECIP && alpha > 0.0f) ? 1.0 / static_cast<double>(alpha) : 0.0;
   for (int m = 0; m < n; ++m) {
-    asm volatile("" : "+v"(x[m]), "+v"(act[m]));  // one division in flight at a time
+    if (!RECIP) asm volatile("" : "+v"(x[m]), "+v"(act[m]));
     float ws = 0.0f;
     if (alpha > 0.0f) {
       const float diff = x[m] - beta;
-      ws = diff / alpha;
+      ws = RECIP ? static_cast<float>(static_cast<double>(diff) * rinv) : diff / alpha;
     }
     const float a = (wmode == 0) ? alpha * act[m] : (wmode == 1 ? act[m] : 1.0f);
     if (!is_finite(a) || a > kAMax || !is_finite(a * ws)) bad = true;
@@ -534,7 +545,7 @@ __device__ __forceinline__ void scale_narrow(float (&x)[E], float (&act)[E], con
       mx = fmaxf(mx, x[lg * G + m]);
     }
     if (valid) {
-      finish_group<MODE>(mn, mx, sp, &x[lg * G], &act[lg * G], G, bad, M, row,
+      finish_group<MODE, false>(mn, mx, sp, &x[lg * G], &act[lg * G], G, bad, M, row,
                          (col0 + lg * G) / g, n_groups, true);
     } else {
 #pragma unroll
@@ -590,7 +601,7 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], const
     __syncthreads();
   }
   if (valid) {
-    finish_group<MODE>(mn, mx, sp, x, act, E, bad, M, row, col0 / g, K / g, (col0 % g) == 0);
+    finish_group<MODE, true>(mn, mx, sp, x, act, E, bad, M, row, col0 / g, K / g, (col0 % g) == 0);
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
@@ -778,17 +789,6 @@ __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int 
   return build_structure(S, k, G, off, lane, t, tc, sv, si);
 }
 
-__device__ __forceinline__ float block_max(float v, Smem& S, int lane, int wave, int nw,
-                                           int parity) {
-  v = wave_max(v);
-  if (nw == 1) return v;
-  if (lane == 0) S.fred[parity][wave] = v;
-  __syncthreads();
-  float r = S.fred[parity][0];
-  for (int w = 1; w < nw; ++w) r = fmaxf(r, S.fred[parity][w]);
-  return r;
-}
-
 __device__ __forceinline__ double block_sum_f64(double v, Smem& S, int lane, int wave, int nw) {
   v = wave_sum_f64(v);
   if (nw == 1) return v;
@@ -889,13 +889,37 @@ void any4_rows_kernel(const LaunchArgs args) {
   }
 
   // a row is rejected when any lane found a bad value (per-wave votes in LDS; the
-  // runtime's block vote would add static shared memory in front of the dynamic one)
+  // runtime's block vote would add static shared memory in front of the dynamic one).
+  // The same exchange carries the row's largest sample weight and the range of its
+  // scaled weights, which set the k-means++ sampling scales.
   if (tid == 0) S.x0 = xv[0];
+  float l_amax = 0.0f, l_xmin = __builtin_huge_valf(), l_xmax = -__builtin_huge_valf();
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    if (m < n_valid) {
+      l_amax = fmaxf(l_amax, av[m]);
+      l_xmin = fminf(l_xmin, xv[m]);
+      l_xmax = fmaxf(l_xmax, xv[m]);
+    }
+  }
+  l_amax = wave_max(l_amax);
+  l_xmin = wave_min(l_xmin);
+  l_xmax = wave_max(l_xmax);
   const bool wave_bad = __ballot(bad) != 0ull;
-  if (lane == 0) S.bad[wave] = wave_bad ? 1 : 0;
+  if (lane == 0) {
+    S.bad[wave] = wave_bad ? 1 : 0;
+    S.rstat[0][wave] = l_amax;
+    S.rstat[1][wave] = l_xmin;
+    S.rstat[2][wave] = l_xmax;
+  }
   __syncthreads();
   bool row_bad = false;
-  for (int w = 0; w < nw; ++w) row_bad = row_bad || S.bad[w] != 0;
+  float a_max = 0.0f;
+  for (int w = 0; w < nw; ++w) {
+    row_bad = row_bad || S.bad[w] != 0;
+    a_max = fmaxf(a_max, S.rstat[0][w]);
+  }
+  a_max = uniform_f(a_max);
   if (row_bad) {
     if (MODE == MODE_FULL) {
       for (int m = 0; m < E; m += 2)
@@ -959,30 +983,76 @@ void any4_rows_kernel(const LaunchArgs args) {
     static_assert(!kPvLds || E * kWave * sizeof(float) <= kBinBytesPerWave, "weights fit the bins");
     SeedWeights<E, kPvLds> pv;
     pv.l = reinterpret_cast<float*>(smem_raw + kSmemHdr + kTableBytes + wave * kBinBytesPerWave) + lane;
-    float lmax = 0.0f;  // this lane's largest sampling weight for the coming draw
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-      pv[m] = av[m];
-      lmax = fmaxf(lmax, pv[m]);
+    for (int m = 0; m < E; ++m) pv[m] = av[m];
+    // Integer CDF terms floor(p * 2^ksc), ksc = 40 - floor(log2 B), for a bound B of the
+    // draw's weights: the largest sample weight for the first draw, and one bound for all
+    // later draws, fixed after the first pick (below).  B = 0 leaves every term 0 and the
+    // centre is copied.
+    int ksc = 0;
+    bool live = a_max > 0.0f;
+    if (live) {
+      int e2;
+      frexpf(a_max, &e2);
+      ksc = 40 - (e2 - 1);
     }
     __syncthreads();
+    float ct = 0.0f, c_first = 0.0f;  // the previous centre and centre 0 (uniform)
+    int pick = -1;
     for (int t = 0; t < k; ++t) {
-      const float pmax = block_max(lmax, S, lane, wave, nw, t & 1);
-      float ct;
-      int pick;
-      if (pmax == 0.0f) {
-        ct = (t == 0) ? S.x0 : S.c[0];
-        pick = -1;
-      } else {
-        int e2;
-        frexpf(pmax, &e2);
-        // each term floor(p * 2^ksc), ksc = 40 - floor(log2 pmax), taken in fp32: the
-        // power-of-two scale is exact (p * 2^ksc < 2^41; a result that underflows is below
-        // 1 and floors to 0 either way) and so is the floor, then widened to fp64 exactly
-        const int ksc = 40 - (e2 - 1);
-        double lsum = static_cast<double>(floorf(ldexpf(pv[0], ksc)));
+      if (t == 1 && init != INIT_RANDOM) {
+        // no later weight a_j * D_j exceeds max_j a_j * m^2, m the larger distance from
+        // centre 0 to the row's extremes (D only decreases; rounding is monotone)
+        float x_min = S.rstat[1][0], x_max = S.rstat[2][0];
+        for (int w = 1; w < nw; ++w) {
+          x_min = fminf(x_min, S.rstat[1][w]);
+          x_max = fmaxf(x_max, S.rstat[2][w]);
+        }
+        const float up = uniform_f(x_max) - c_first, down = c_first - uniform_f(x_min);
+        const float mm = up > down ? up : down;
+        const float bound = a_max * (mm * mm);
+        live = bound > 0.0f;
+        if (live) {
+          int e2;
+          frexpf(bound, &e2);
+          ksc = 40 - (e2 - 1);
+        }
+      }
+      // This draw's sampling weights, then their CDF terms.  For t >= 1 the weights are
+      // a_j * min_t fl((w_S_j - c_t)^2), updated from the previous centre.
+      // They are never NaN and never below zero (a zero may be -0), so the float order is
+      // the order of their bit patterns as signed integers: the min runs as an integer op,
+      // which needs no NaN quieting of its operands.  Each term floor(p * 2^ksc) is taken
+      // in fp32: the power-of-two scale is exact (p * 2^ksc < 2^41; a result that
+      // underflows is below 1 and floors to 0 either way) and so is the floor, then
+      // widened to fp64 exactly (a lane's sum stays below 2^46).
+      if (t > 0 && init == INIT_RANDOM) {
+        // random initialization (Appendix C.2): the drawn element leaves the pool, the
+        // others keep their weight a_j
+        const int pm = pick - tid * E;  // no draw (pick < 0) never matches
 #pragma unroll
-        for (int m = 1; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
+        for (int m = 0; m < E; ++m)
+          if (m == pm) pv[m] = 0.0f;
+      } else if (t == 1) {
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          float d = xv[m] - ct;
+          d = d * d;
+          pv[m] = av[m] * d;
+        }
+      } else if (t > 1) {
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          float d = xv[m] - ct;
+          d = d * d;
+          const int pd = __float_as_int(av[m] * d);
+          pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
+        }
+      }
+      double lsum = static_cast<double>(floorf(ldexpf(pv[0], ksc)));
+#pragma unroll
+      for (int m = 1; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
+      if (!live) lsum = 0.0;
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
         const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
@@ -997,6 +1067,12 @@ void any4_rows_kernel(const LaunchArgs args) {
           }
         }
         const unsigned long long excl = woff + incl - ls;
+      if (Q == 0) {
+        // every weight is 0, or below the scale's resolution: copy (w_S[0] for the first
+        // centre, centre 0 after that)
+        ct = (t == 0) ? uniform_f(S.x0) : c_first;
+        pick = -1;
+      } else {
         // greedy k-means++ searches several candidates (s >= 1 land in S.gk); the plain
         // draw is candidate 0
         const int n_cand = (init == INIT_GREEDY && t > 0) ? greedy_trials(k) : 1;
@@ -1037,8 +1113,8 @@ void any4_rows_kernel(const LaunchArgs args) {
           }
           __syncthreads();
         }
-        ct = S.pick_c;
-        pick = S.pick_j;
+        ct = uniform_f(S.pick_c);
+        pick = __builtin_amdgcn_readfirstlane(S.pick_j);
         if (n_cand > 1) {
           // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * 2^ksc): exact
           // integers (per lane below 2^47 in fp64, per row in u64), compared exactly
@@ -1076,40 +1152,7 @@ void any4_rows_kernel(const LaunchArgs args) {
         S.c[t] = ct;
         S.picks[t] = pick;
       }
-      if (t == k - 1) break;  // the last centroid needs no further sampling weights
-      // sampling weights for the next draw: a_j * min_t fl((w_S_j - c_t)^2).  They are
-      // never NaN and never below zero (a zero may be -0), so the float order is the
-      // order of their bit patterns as signed integers: min and max run as integer ops,
-      // which need no NaN quieting of their operands.
-      int imax = 0;
-      if (init == INIT_RANDOM) {
-        // random initialization (Appendix C.2): the drawn element leaves the pool, the
-        // others keep their weight a_j
-        const int pm = pick - tid * E;  // no draw (pick < 0) never matches
-#pragma unroll
-        for (int m = 0; m < E; ++m) {
-          if (m == pm) pv[m] = 0.0f;
-          imax = max(imax, __float_as_int(pv[m]));
-        }
-      } else if (t == 0) {
-#pragma unroll
-        for (int m = 0; m < E; ++m) {
-          float d = xv[m] - ct;
-          d = d * d;
-          pv[m] = av[m] * d;
-          imax = max(imax, __float_as_int(pv[m]));
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < E; ++m) {
-          float d = xv[m] - ct;
-          d = d * d;
-          const int pd = __float_as_int(av[m] * d);
-          pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
-          imax = max(imax, __float_as_int(pv[m]));
-        }
-      }
-      lmax = __int_as_float(imax);
+      if (t == 0) c_first = ct;
     }
     __syncthreads();
     if (MODE == MODE_SEED) {
