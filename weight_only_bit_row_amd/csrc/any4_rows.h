@@ -1040,7 +1040,7 @@ void any4_rows_kernel(const LaunchArgs args) {
           d = d * d;
           pv[m] = av[m] * d;
         }
-      } else if (t > 1) {
+      } else if (t > 1 && !kPvLds) {
 #pragma unroll
         for (int m = 0; m < E; ++m) {
           float d = xv[m] - ct;
@@ -1049,9 +1049,24 @@ void any4_rows_kernel(const LaunchArgs args) {
           pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
         }
       }
-      double lsum = static_cast<double>(floorf(ldexpf(pv[0], ksc)));
+      double lsum = 0.0;
+      if (t > 1 && kPvLds && init != INIT_RANDOM) {
+        // weights in LDS: the update and the CDF term in one pass, one read and one
+        // write of each weight (in registers the two passes stay apart, which keeps the
+        // register pressure of the fused pass off the seeding loop)
 #pragma unroll
-      for (int m = 1; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
+        for (int m = 0; m < E; ++m) {
+          float d = xv[m] - ct;
+          d = d * d;
+          const int pd = __float_as_int(av[m] * d);
+          const float p = __int_as_float(min(__float_as_int(pv[m]), pd));
+          pv[m] = p;
+          lsum += static_cast<double>(floorf(ldexpf(p, ksc)));
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
+      }
       if (!live) lsum = 0.0;
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
         const unsigned long long incl = wave_incl_scan_u64(ls);
