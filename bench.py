@@ -38,7 +38,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-KERNEL_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_kernels.hip")
+# the row kernel's source: its device code and the translation unit of the instance the
+# headline workload runs (32 elements per lane, up to 8 waves)
+KERNEL_SRC = (os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_rows.h"),
+              os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_rows_e32_w8.hip"))
 COUNTERS = os.path.join(ROOT, "profiles", "any4_rows_up_proj_counters.md")
 BOOKENDS_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_bookends.hip")
 BOOKENDS_COUNTERS = os.path.join(ROOT, "profiles", "any4_bookends_calib32x2048_up_proj.md")
@@ -55,11 +58,14 @@ def credited_flops_per_element(k: int, iters: int) -> int:
     return 6 + 4 * k + iters * (3 * k + 1) + (3 * k + 2)
 
 
-def kernel_source_hash(path: str = KERNEL_SRC) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(paths=KERNEL_SRC) -> str:
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(counters: str = COUNTERS, src: str = KERNEL_SRC, key: str = "traffic_bytes_per_launch"):
+def load_traffic(counters: str = COUNTERS, src=KERNEL_SRC, key: str = "traffic_bytes_per_launch"):
     """HBM bytes per launch from a committed counter summary, if it was taken on the
     current kernel source; otherwise None."""
     if not os.path.exists(counters):
@@ -295,7 +301,7 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
          "workload": f"one calibration token times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv1, "bf16_matmul_ms_per_call": ms_mm1,
          "roofline": roof(bytes_gv(1), ms_gv1, "gemv1_traffic_bytes_per_launch")},
-        {"kernel": "any4_lut_gemv (gemv_kernel<8, bf16 x, 2 rows per wave>)",
+        {"kernel": "any4_lut_gemv (gemv_mfma_kernel<4>, bf16 MFMA, 16 rows per workgroup)",
          "workload": f"eight calibration tokens times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv8, "bf16_matmul_ms_per_call": ms_mm8,
          "roofline": roof(bytes_gv(8), ms_gv8, "gemv8_traffic_bytes_per_launch")},

@@ -265,13 +265,17 @@ def _check_gemv(q, g, k, codes, lut, scale, offset, x, dtype, name):
     return float((err / np.maximum(s[~nan], 1e-300)).max()) if err.size else 0.0
 
 
-# (name, N, K, group, k, M, x dtype, seed): one to eight tokens, one and several x slices
+# (name, N, K, group, k, M, x dtype, seed): one to eight tokens, one and several x slices;
+# bf16 x of five or more tokens with groups of 32 or more runs on the matrix cores, the
+# rest on the VALU kernel
 GEMV_RANDOM = [
     ("m1_k4096_bf16", 40, 4096, 128, 16, 1, BF16, 11),
     ("m3_k512_f32", 33, 512, 64, 8, 3, F32, 12),
     ("m5_k2048_bf16_g16", 17, 2048, 16, 16, 5, BF16, 13),
     ("m8_k28672_bf16", 9, 28672, 128, 16, 8, BF16, 14),
     ("m2_k6160_f32_codes_past_lut", 21, 6160, 16, 4, 2, F32, 15),
+    ("m6_k4096_bf16_g64_codes_past_lut", 19, 4096, 64, 8, 6, BF16, 16),
+    ("m7_k2048_bf16_g32", 50, 2048, 32, 16, 7, BF16, 17),
 ]
 
 

@@ -589,6 +589,196 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
   }
 }
 
+// ---------------------------------------------------------------------------------
+// The LUT product on the matrix cores, for bf16 activations and groups a multiple of 32
+// columns.  With Eq. 4's w_hat = alpha * L[q] + beta, the columns j of one block (inside
+// one group g) of row i give
+//   sum_j x[t][j] * w_hat[i][j] = alpha_ig * sum_j x[t][j] L_i[q_ij] + beta_ig * sum_j x[t][j].
+// The row's fp16 LUT values are split exactly into two bf16 parts, L = Lh + Ll (an fp16
+// value has 11 significant bits, bf16 8, so the remainder needs at most 4), and the sums
+// come from v_mfma_f32_16x16x32_bf16: products of bf16 values are exact in fp32 and
+// accumulate in fp32, the arithmetic of the VALU kernel up to the summation order.
+//
+// A workgroup of 4 waves takes a tile of 16 rows; wave w takes the w-th quarter of the
+// row's blocks of 32 NMF columns (NMF = 1, 2, 4 for groups of 32, 64 and 128 or more),
+// and the four partial results are added in LDS in wave order (a fixed order, so
+// repeated calls give the same bits).  In a block, lane l holds tile row i = l % 16 and
+// the 8 NMF consecutive columns that lane group h = l / 16 owns; MFMA s (s < NMF) takes 8
+// of them, in both operands, so the sums over k cover every column of the block once:
+//   A (16 x 32, bf16): token t = l % 16 of x at those columns (rows t >= n_tokens repeat
+//       the last token: their outputs are not stored)
+//   B (32 x 16, bf16): row i's Lh (or Ll) at those columns' codes, or 1 for the x sums
+//   C (16 x 16, fp32): lane l holds tokens 4 (l / 16) + r, r < 4, of row l % 16
+// and y[t][i] += alpha_ig * (C_Lh + C_Ll) + beta_ig * C_S per block, in fp32.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMfRows = 16;    // rows per workgroup tile
+constexpr int kMfWaves = 4;    // K slices per tile (waves per workgroup)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite values; NaN stays NaN)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0x7FFFFFu) ? 0x40u : 0u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Each lane's data for one block of 32 * NMF columns: its codes (NMF 4-byte words) and its
+// token's x (NMF 16-byte vectors), and the alpha/beta bits of the block's group.
+template <int NMF>
+struct MfBlock {
+  uint32_t w[NMF];
+  u32x4 x[NMF];
+  uint16_t a, b;
+};
+
+template <int NMF>
+__global__ __launch_bounds__(kMfWaves * 64) void gemv_mfma_kernel(const GemvDesc d) {
+  constexpr int BC = 32 * NMF;   // columns per block; lane group h takes BC / 4 of them
+  // Lane l's LUT entry q, for its row l % 16, at word q * 64 + l: Lh bits | Ll bits << 16
+  // (a code past the LUT: Lh NaN, Ll 0).  A lane only reads its own column, so every read
+  // of a wave hits 64 distinct banks whatever the codes (no bank conflicts); the waves of
+  // the workgroup map lanes to rows the same way and share the table.
+  __shared__ __attribute__((aligned(1024))) uint32_t ltab[16][64];
+  __shared__ mf32x4_t part[kMfWaves][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t N = d.n_rows, K = d.n_cols;
+  const int64_t row0 = int64_t(blockIdx.x) * kMfRows;
+  const int64_t n_blocks = K / BC;
+  const int64_t per = (n_blocks + kMfWaves - 1) / kMfWaves;
+  const int64_t b_begin = wave * per < n_blocks ? wave * per : n_blocks;
+  const int64_t b_end = b_begin + per < n_blocks ? b_begin + per : n_blocks;
+  const int i = lane & 15, h = lane >> 4;
+  const int64_t row = row0 + i < N ? row0 + i : N - 1;   // tail rows read row N-1, never stored
+  // this lane's token in operand A; rows of A past the last token repeat it (their outputs
+  // are never stored), so every lane loads without a branch
+  const int t = (lane & 15) < d.n_tokens ? (lane & 15) : static_cast<int>(d.n_tokens) - 1;
+  const uint16_t* x = static_cast<const uint16_t*>(d.x) + t * K;
+  const uint8_t* codes = d.codes + row * (K >> 1);
+  const int gshift = __builtin_ctz(static_cast<uint32_t>(d.group));
+  const int64_t n_groups = K >> gshift;
+  const uint16_t* scale = d.scale + row * n_groups;
+  const uint16_t* offset = d.offset + row * n_groups;
+  const int64_t b_last = b_end > b_begin ? b_end - 1 : b_begin;   // clamp for prefetches
+  // columns of a row are below 2^31 (checked by the ABI), so offsets within a row are 32-bit
+  auto load = [&](MfBlock<NMF>& m, int64_t b) {
+    const uint32_t c = static_cast<uint32_t>(b) * BC + (BC / 4) * h;   // lane's first column
+    if constexpr (NMF == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(codes + (c >> 1));
+      m.w[0] = v.x; m.w[1] = v.y; m.w[2] = v.z; m.w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int s = 0; s < NMF; ++s) m.w[s] = *reinterpret_cast<const uint32_t*>(codes + (c >> 1) + 4 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < NMF; ++s) m.x[s] = *reinterpret_cast<const u32x4*>(x + c + 8 * s);
+    const uint32_t g = (static_cast<uint32_t>(b) * BC) >> gshift;
+    m.a = scale[g];
+    m.b = offset[g];
+  };
+  // the first two blocks' loads go out with the LUT loads, before the tables are built
+  MfBlock<NMF> b0, b1, b2;
+  if (b_begin < b_end) {
+    load(b0, b_begin);
+    load(b1, b_begin + 1 < b_last ? b_begin + 1 : b_last);
+  }
+  // the table's 1024 words, 1024 / (64 kMfWaves) per thread: all LUT loads are issued
+  // before any is used (one wait)
+  constexpr int kPer = 16 * 64 / (kMfWaves * 64);
+  uint16_t lbits[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int n = tid + u * kMfWaves * 64;
+    const int q = n >> 6, ti = n & 15;      // entry q of lane column n % 64, row n % 16
+    const int64_t trow = row0 + ti < N ? row0 + ti : N - 1;
+    lbits[u] = d.lut[trow * d.n_clusters + (q < d.n_clusters ? q : 0)];
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int n = tid + u * kMfWaves * 64;
+    const int q = n >> 6;
+    uint32_t e = 0x7FC0u;                   // past the LUT: NaN, 0
+    if (q < d.n_clusters) {
+      const float L = half_bits_to_float(lbits[u]);
+      const uint32_t hb = bf16_rne_bits(L);
+      const float lo = L - __uint_as_float(hb << 16);   // exact: at most 4 significant bits
+      e = hb | ((__float_as_uint(lo) >> 16) << 16);
+    }
+    ltab[q][n & 63] = e;
+  }
+  __syncthreads();                                       // the LUT table is ready
+  // byte address of entry q of this lane: q << 8 | 4 lane, byte 1 from a nibble, byte 0
+  // the lane's column (one v_perm per lookup)
+  const uint32_t lane4 = 4u * static_cast<uint32_t>(lane);
+  const char* tbytes = reinterpret_cast<const char*>(&ltab[0][0]);
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  mf32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+  // one block: its LUT operands from the byte table, three MFMA chains (x*Lh, x*Ll, x*1),
+  // then y += alpha * (C_Lh + C_Ll) + beta * C_S
+  auto compute = [&](const MfBlock<NMF>& cur) {
+    mf32x4_t ch = {0.0f, 0.0f, 0.0f, 0.0f}, cl = {0.0f, 0.0f, 0.0f, 0.0f};
+    mf32x4_t cs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NMF; ++s) {
+      const uint32_t w = cur.w[s];
+      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 2p, 2p + 1
+      u32x4 bh, bl;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {                 // code byte p: columns 2p and 2p + 1
+        const uint32_t sel = 0x0C0C0000u | ((4u + p) << 8);
+        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tbytes + __builtin_amdgcn_perm(lo, lane4, sel));
+        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tbytes + __builtin_amdgcn_perm(hi, lane4, sel));
+        bh[p] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);   // (Lh of column 2p, 2p + 1)
+        bl[p] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);   // (Ll of column 2p, 2p + 1)
+      }
+      const bf16x8_t a = as_bf16x8(cur.x[s]);
+      ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bh), ch, 0, 0, 0);
+      cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), cs, 0, 0, 0);
+      cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bl), cl, 0, 0, 0);
+    }
+    const float al = half_bits_to_float(cur.a), be = half_bits_to_float(cur.b);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = fmaf(be, cs[r], fmaf(al, ch[r] + cl[r], y[r]));
+  };
+  // Three buffers in rotation, loads two blocks ahead.  The rotation is unrolled rather
+  // than copied: a copy of a buffer whose loads are in flight would wait for them.
+  auto step = [&](const MfBlock<NMF>& cur, MfBlock<NMF>& fill, int64_t b) {
+    load(fill, b + 2 < b_last ? b + 2 : b_last);
+    __builtin_amdgcn_sched_barrier(0);  // the later block's loads go out before this one's math
+    compute(cur);
+  };
+  for (int64_t b = b_begin; b < b_end; b += 3) {
+    step(b0, b2, b);
+    if (b + 1 < b_end) step(b1, b0, b + 1);
+    if (b + 2 < b_end) step(b2, b1, b + 2);
+  }
+  part[wave][lane] = y;
+  __syncthreads();
+  if (wave != 0) return;
+  mf32x4_t acc = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < kMfWaves; ++w) {
+    const mf32x4_t v = part[w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += v[r];
+  }
+  // lane l holds tokens 4 (l / 16) + r of row l % 16
+  if (row0 + i < N) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * h + r;
+      if (tok < d.n_tokens) d.y[int64_t(tok) * N + row0 + i] = acc[r];
+    }
+  }
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
@@ -659,6 +849,18 @@ hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
 
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
+  // bf16 activations and groups of whole 32-column MFMA steps go to the matrix cores
+  if (d.x_bf16 && d.group % 32 == 0 && d.n_tokens >= kGemvMfmaMinTokens && aligned(d.x, 16) &&
+      aligned(d.codes, 16)) {
+    const dim3 grid(static_cast<uint32_t>((d.n_rows + kMfRows - 1) / kMfRows));
+    if (d.group == 32)
+      hipLaunchKernelGGL((gemv_mfma_kernel<1>), grid, dim3(kMfWaves * 64), 0, stream, d);
+    else if (d.group == 64)
+      hipLaunchKernelGGL((gemv_mfma_kernel<2>), grid, dim3(kMfWaves * 64), 0, stream, d);
+    else
+      hipLaunchKernelGGL((gemv_mfma_kernel<4>), grid, dim3(kMfWaves * 64), 0, stream, d);
+    return hipGetLastError();
+  }
   const bool short_rows = d.n_cols <= kGvLongK;
   if (d.n_tokens <= 1)
     return short_rows ? launch_gemv_mt<1, 2>(d, stream) : launch_gemv_mt<1, 4>(d, stream);

@@ -177,6 +177,8 @@ struct GemvDesc {
   int32_t pad_;
 };
 constexpr int kGemvMaxTokens = 8;
+// token counts from which bf16 activations use the matrix-core kernel (measured)
+constexpr int kGemvMfmaMinTokens = 5;
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream);
 
 }  // namespace any4
