@@ -301,7 +301,7 @@ def bookends(any4, torch, np, q, N, K, g, k, dev, stream, profile_steps=0):
          "workload": f"one calibration token times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv1, "bf16_matmul_ms_per_call": ms_mm1,
          "roofline": roof(bytes_gv(1), ms_gv1, "gemv1_traffic_bytes_per_launch")},
-        {"kernel": "any4_lut_gemv (gemv_mfma_kernel<4>, bf16 MFMA, 16 rows per workgroup)",
+        {"kernel": "any4_lut_gemv (gemv_mfma_kernel<4, 4>, bf16 MFMA, 32 rows per workgroup)",
          "workload": f"eight calibration tokens times the quantized {N}x{K} up_proj, fp32 out",
          "ms_per_call": ms_gv8, "bf16_matmul_ms_per_call": ms_mm8,
          "roofline": roof(bytes_gv(8), ms_gv8, "gemv8_traffic_bytes_per_launch")},

@@ -266,7 +266,7 @@ def _check_gemv(q, g, k, codes, lut, scale, offset, x, dtype, name):
 
 
 # (name, N, K, group, k, M, x dtype, seed): one to eight tokens, one and several x slices;
-# bf16 x of five or more tokens with groups of 32 or more runs on the matrix cores, the
+# bf16 x of three or more tokens with groups of 32 or more runs on the matrix cores, the
 # rest on the VALU kernel
 GEMV_RANDOM = [
     ("m1_k4096_bf16", 40, 4096, 128, 16, 1, BF16, 11),

@@ -599,21 +599,32 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvDesc d, int sp
 // come from v_mfma_f32_16x16x32_bf16: products of bf16 values are exact in fp32 and
 // accumulate in fp32, the arithmetic of the VALU kernel up to the summation order.
 //
-// A workgroup of 4 waves takes a tile of 16 rows; wave w takes the w-th quarter of the
-// row's blocks of 32 NMF columns (NMF = 1, 2, 4 for groups of 32, 64 and 128 or more),
-// and the four partial results are added in LDS in wave order (a fixed order, so
-// repeated calls give the same bits).  In a block, lane l holds tile row i = l % 16 and
-// the 8 NMF consecutive columns that lane group h = l / 16 owns; MFMA s (s < NMF) takes 8
-// of them, in both operands, so the sums over k cover every column of the block once:
-//   A (16 x 32, bf16): token t = l % 16 of x at those columns (rows t >= n_tokens repeat
-//       the last token: their outputs are not stored)
-//   B (32 x 16, bf16): row i's Lh (or Ll) at those columns' codes, or 1 for the x sums
+// The reduction index k of the L sums runs over (column, part) pairs: operand B holds
+// (Lh, Ll) of a column in two neighbouring k slots, which is one lookup of a table entry
+// stored as Lh | Ll << 16, and operand A holds that column's x twice.  So one MFMA covers
+// 16 columns, lane l holding 4 of them:
+//   A (16 x 32, bf16): token t = l % 16, (x_c, x_c) for each of the lane's columns c (rows
+//       t >= n_tokens repeat the last token: their outputs are not stored)
+//   B (32 x 16, bf16): row i = l % 16's (Lh, Ll) at those columns' codes
 //   C (16 x 16, fp32): lane l holds tokens 4 (l / 16) + r, r < 4, of row l % 16
-// and y[t][i] += alpha_ig * (C_Lh + C_Ll) + beta_ig * C_S per block, in fp32.
+// and the x sums take one more MFMA per 32 columns with x in plain order against ones.
+// Per block, y[t][i] += alpha_ig * C_L + beta_ig * C_S in fp32.
+//
+// A workgroup takes two tiles of 16 rows, and its W waves (W = 2, 4 or 8, by row length)
+// split the row's blocks of 32 NMF columns (NMF = 1, 2, 4 for groups of 32, 64 and 128 or
+// more) into W contiguous ranges; the W partial results are added in LDS in wave order (a
+// fixed order, so repeated calls give the same bits).  In a block, lane l holds row
+// i = l % 16 of each tile and the 8 NMF consecutive columns that lane group h = l / 16
+// owns.  The x operand and the x sums serve both tiles.  All loads are buffer loads with
+// per-lane offsets fixed for the whole call and the block's offset in a scalar register.
+// The alpha/beta pairs are loaded once per four blocks (lane group h holds block h's pair
+// for its rows) and reach the other lanes through ds_bpermute.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kMfRows = 16;    // rows per workgroup tile
-constexpr int kMfWaves = 4;    // K slices per tile (waves per workgroup)
+constexpr int kMfTiles = 2;                  // 16-row tiles per workgroup
+constexpr int kMfRows = 16 * kMfTiles;       // rows per workgroup
+constexpr int64_t kMfMaxCols = int64_t(1) << 26;   // per-lane buffer offsets stay 32-bit
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource word 3 on gfx9 parts
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) {
   bf16x8_t r;
@@ -628,153 +639,217 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Each lane's data for one block of 32 * NMF columns: its codes (NMF 4-byte words) and its
-// token's x (NMF 16-byte vectors), and the alpha/beta bits of the block's group.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t n = bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+                                           kRawBufferWord3);
+}
+
+// Each lane's data for one block of 32 * NMF columns: its codes in each tile (NMF 4-byte
+// words) and its token's x (NMF 16-byte vectors).
 template <int NMF>
 struct MfBlock {
-  uint32_t w[NMF];
+  uint32_t w[kMfTiles][NMF];
   u32x4 x[NMF];
-  uint16_t a, b;
 };
 
-template <int NMF>
-__global__ __launch_bounds__(kMfWaves * 64) void gemv_mfma_kernel(const GemvDesc d) {
+template <int NMF, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const GemvDesc d) {
   constexpr int BC = 32 * NMF;   // columns per block; lane group h takes BC / 4 of them
-  // Lane l's LUT entry q, for its row l % 16, at word q * 64 + l: Lh bits | Ll bits << 16
-  // (a code past the LUT: Lh NaN, Ll 0).  A lane only reads its own column, so every read
-  // of a wave hits 64 distinct banks whatever the codes (no bank conflicts); the waves of
-  // the workgroup map lanes to rows the same way and share the table.
-  __shared__ __attribute__((aligned(1024))) uint32_t ltab[16][64];
-  __shared__ mf32x4_t part[kMfWaves][64];
+  // Lane l's LUT entry q, for row l % 16 of tile T, at word (16 T + q) * 64 + l: Lh bits |
+  // Ll bits << 16 (a code past the LUT: Lh NaN, Ll 0).  A lane only reads its own column,
+  // so every read of a wave hits 64 distinct banks whatever the codes (no bank
+  // conflicts); all waves map lanes to rows the same way and share the table.
+  __shared__ __attribute__((aligned(1024))) uint32_t ltab[kMfTiles][16][64];
+  __shared__ mf32x4_t part[NW][kMfTiles][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t N = d.n_rows, K = d.n_cols;
   const int64_t row0 = int64_t(blockIdx.x) * kMfRows;
   const int64_t n_blocks = K / BC;
-  const int64_t per = (n_blocks + kMfWaves - 1) / kMfWaves;
+  const int64_t per = (n_blocks + NW - 1) / NW;
   const int64_t b_begin = wave * per < n_blocks ? wave * per : n_blocks;
   const int64_t b_end = b_begin + per < n_blocks ? b_begin + per : n_blocks;
+  // every load is unconditional, its block clamped to the wave's range (a wave with no
+  // blocks reads the row's last one): loads under a branch make the compiler wait for
+  // every load in flight where the branches join
+  const int64_t b_last = b_end > b_begin ? b_end - 1 : n_blocks - 1;
   const int i = lane & 15, h = lane >> 4;
-  const int64_t row = row0 + i < N ? row0 + i : N - 1;   // tail rows read row N-1, never stored
   // this lane's token in operand A; rows of A past the last token repeat it (their outputs
   // are never stored), so every lane loads without a branch
   const int t = (lane & 15) < d.n_tokens ? (lane & 15) : static_cast<int>(d.n_tokens) - 1;
-  const uint16_t* x = static_cast<const uint16_t*>(d.x) + t * K;
-  const uint8_t* codes = d.codes + row * (K >> 1);
   const int gshift = __builtin_ctz(static_cast<uint32_t>(d.group));
   const int64_t n_groups = K >> gshift;
-  const uint16_t* scale = d.scale + row * n_groups;
-  const uint16_t* offset = d.offset + row * n_groups;
-  const int64_t b_last = b_end > b_begin ? b_end - 1 : b_begin;   // clamp for prefetches
-  // columns of a row are below 2^31 (checked by the ABI), so offsets within a row are 32-bit
-  auto load = [&](MfBlock<NMF>& m, int64_t b) {
-    const uint32_t c = static_cast<uint32_t>(b) * BC + (BC / 4) * h;   // lane's first column
-    if constexpr (NMF == 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(codes + (c >> 1));
-      m.w[0] = v.x; m.w[1] = v.y; m.w[2] = v.z; m.w[3] = v.w;
-    } else {
+  // buffers based at the workgroup's first row; tail rows read row N - 1, never stored
+  const uint32_t half_k = static_cast<uint32_t>(K >> 1);
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(d.codes + row0 * (K >> 1), uint64_t(N - row0) * half_k);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(d.scale + row0 * n_groups, uint64_t(N - row0) * n_groups * 2);
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(d.offset + row0 * n_groups, uint64_t(N - row0) * n_groups * 2);
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(d.x, uint64_t(d.n_tokens) * K * 2);
+  uint32_t voff_c[kMfTiles], voff_p[kMfTiles];
 #pragma unroll
-      for (int s = 0; s < NMF; ++s) m.w[s] = *reinterpret_cast<const uint32_t*>(codes + (c >> 1) + 4 * s);
+  for (int T = 0; T < kMfTiles; ++T) {
+    const int64_t r = row0 + 16 * T + i;
+    const uint32_t rr = static_cast<uint32_t>((r < N ? r : N - 1) - row0);
+    voff_c[T] = rr * half_k + (BC / 8) * h;
+    voff_p[T] = rr * static_cast<uint32_t>(n_groups) * 2;
+  }
+  const uint32_t voff_x = static_cast<uint32_t>(t) * static_cast<uint32_t>(K) * 2 + (BC / 4) * h * 2;
+  auto load = [&](MfBlock<NMF>& m, int64_t b) {
+    const int bc = static_cast<int>(b) * (BC / 2);   // the block's byte offset in a code row
+#pragma unroll
+    for (int T = 0; T < kMfTiles; ++T) {
+      if constexpr (NMF == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, voff_c[T], bc, 0);
+        m.w[T][0] = v.x; m.w[T][1] = v.y; m.w[T][2] = v.z; m.w[T][3] = v.w;
+      } else {
+#pragma unroll
+        for (int s = 0; s < NMF; ++s) m.w[T][s] = __builtin_amdgcn_raw_buffer_load_b32(rc, voff_c[T] + 4 * s, bc, 0);
+      }
     }
 #pragma unroll
-    for (int s = 0; s < NMF; ++s) m.x[s] = *reinterpret_cast<const u32x4*>(x + c + 8 * s);
-    const uint32_t g = (static_cast<uint32_t>(b) * BC) >> gshift;
-    m.a = scale[g];
-    m.b = offset[g];
+    for (int s = 0; s < NMF; ++s) m.x[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x + 16 * s, 4 * bc, 0);
   };
-  // the first two blocks' loads go out with the LUT loads, before the tables are built
-  MfBlock<NMF> b0, b1, b2;
-  if (b_begin < b_end) {
-    load(b0, b_begin);
-    load(b1, b_begin + 1 < b_last ? b_begin + 1 : b_last);
-  }
-  // the table's 1024 words, 1024 / (64 kMfWaves) per thread: all LUT loads are issued
-  // before any is used (one wait)
-  constexpr int kPer = 16 * 64 / (kMfWaves * 64);
+  // alpha | beta << 16 of block b0 + h (clamped) for this lane's rows
+  auto load_params = [&](uint32_t (&p)[kMfTiles], int64_t b0) {
+    const int64_t b = b0 + h < b_last ? b0 + h : b_last;
+    const uint32_t g2 = ((static_cast<uint32_t>(b) * BC) >> gshift) * 2;
+#pragma unroll
+    for (int T = 0; T < kMfTiles; ++T) {
+      const uint32_t a = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_p[T] + g2, 0, 0);
+      const uint32_t o = __builtin_amdgcn_raw_buffer_load_b16(ro, voff_p[T] + g2, 0, 0);
+      p[T] = (a & 0xFFFFu) | (o << 16);
+    }
+  };
+  // the tables' 2048 words, 2048 / (64 NW) per thread, loaded first; then the first
+  // blocks' loads go out, so that the wait for the LUT words does not wait for them
+  constexpr int kPer = kMfTiles * 16 * 64 / (NW * 64);
   uint16_t lbits[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int n = tid + u * kMfWaves * 64;
-    const int q = n >> 6, ti = n & 15;      // entry q of lane column n % 64, row n % 16
-    const int64_t trow = row0 + ti < N ? row0 + ti : N - 1;
+    const int n = tid + u * NW * 64;
+    const int T = n >> 10, q = (n >> 6) & 15, ti = n & 15;
+    const int64_t r = row0 + 16 * T + ti;
+    const int64_t trow = r < N ? r : N - 1;
     lbits[u] = d.lut[trow * d.n_clusters + (q < d.n_clusters ? q : 0)];
   }
+  // (the first pairs before the first blocks: the loop's first wait is for the pairs)
+  auto clampb = [&](int64_t b) { return b < b_last ? b : b_last; };
+  MfBlock<NMF> b0, b1, b2, b3;
+  uint32_t pc[kMfTiles], pn[kMfTiles];
+  load_params(pn, b_begin);
+  load(b0, clampb(b_begin));
+  load(b1, clampb(b_begin + 1));
+  load(b2, clampb(b_begin + 2));
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int n = tid + u * kMfWaves * 64;
-    const int q = n >> 6;
-    uint32_t e = 0x7FC0u;                   // past the LUT: NaN, 0
-    if (q < d.n_clusters) {
-      const float L = half_bits_to_float(lbits[u]);
-      const uint32_t hb = bf16_rne_bits(L);
-      const float lo = L - __uint_as_float(hb << 16);   // exact: at most 4 significant bits
-      e = hb | ((__float_as_uint(lo) >> 16) << 16);
-    }
-    ltab[q][n & 63] = e;
+    const int n = tid + u * NW * 64;
+    const int T = n >> 10, q = (n >> 6) & 15;
+    // computed for every entry and then selected, so that no load is sunk into a branch
+    const float L = half_bits_to_float(lbits[u]);
+    const uint32_t hb = bf16_rne_bits(L);
+    const float lo = L - __uint_as_float(hb << 16);   // exact: at most 4 significant bits
+    const uint32_t e = hb | ((__float_as_uint(lo) >> 16) << 16);
+    ltab[T][q][n & 63] = q < d.n_clusters ? e : 0x7FC0u;   // past the LUT: NaN, 0
   }
-  __syncthreads();                                       // the LUT table is ready
-  // byte address of entry q of this lane: q << 8 | 4 lane, byte 1 from a nibble, byte 0
-  // the lane's column (one v_perm per lookup)
+  __syncthreads();                                       // the LUT tables are ready
+  // byte address of entry q of this lane in tile 0: q << 8 | 4 lane, byte 1 from a nibble,
+  // byte 0 the lane's column (one v_perm per lookup); tile T adds T * 4096
   const uint32_t lane4 = 4u * static_cast<uint32_t>(lane);
-  const char* tbytes = reinterpret_cast<const char*>(&ltab[0][0]);
+  const char* tbytes = reinterpret_cast<const char*>(&ltab[0][0][0]);
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  mf32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-  // one block: its LUT operands from the byte table, three MFMA chains (x*Lh, x*Ll, x*1),
-  // then y += alpha * (C_Lh + C_Ll) + beta * C_S
-  auto compute = [&](const MfBlock<NMF>& cur) {
-    mf32x4_t ch = {0.0f, 0.0f, 0.0f, 0.0f}, cl = {0.0f, 0.0f, 0.0f, 0.0f};
+  mf32x4_t y[kMfTiles];
+#pragma unroll
+  for (int T = 0; T < kMfTiles; ++T) y[T] = mf32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // one block (j-th of its group of four): every table lookup of the block first, then
+  // the MFMA chains (per tile x * (Lh, Ll), once x * 1), then y += alpha C_L + beta C_S
+  auto compute = [&](const MfBlock<NMF>& cur, int j, bool valid) {
+    uint32_t g[kMfTiles][8 * NMF];     // entry of column c of the lane's 8 NMF
+#pragma unroll
+    for (int T = 0; T < kMfTiles; ++T) {
+      const char* tb = tbytes + T * 4096;
+#pragma unroll
+      for (int s = 0; s < NMF; ++s) {
+        const uint32_t w = cur.w[T][s];
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 2p, 2p + 1
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {                 // code byte p: columns 2p and 2p + 1
+          const uint32_t sel = 0x0C0C0000u | ((4u + p) << 8);
+          g[T][8 * s + 2 * p] = *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(lo, lane4, sel));
+          g[T][8 * s + 2 * p + 1] = *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(hi, lane4, sel));
+        }
+      }
+    }
     mf32x4_t cs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < NMF; ++s) {
-      const uint32_t w = cur.w[s];
-      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 2p, 2p + 1
-      u32x4 bh, bl;
+    for (int s = 0; s < NMF; ++s)
+      cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.x[s]), as_bf16x8(ones), cs, 0, 0, 0);
+    mf32x4_t cl[kMfTiles];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {                 // code byte p: columns 2p and 2p + 1
-        const uint32_t sel = 0x0C0C0000u | ((4u + p) << 8);
-        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tbytes + __builtin_amdgcn_perm(lo, lane4, sel));
-        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tbytes + __builtin_amdgcn_perm(hi, lane4, sel));
-        bh[p] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);   // (Lh of column 2p, 2p + 1)
-        bl[p] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);   // (Ll of column 2p, 2p + 1)
+    for (int T = 0; T < kMfTiles; ++T) cl[T] = mf32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 2 * NMF; ++u) {     // columns 4u .. 4u + 3 of the lane's 8 NMF
+      const u32x4& xs = cur.x[u >> 1];
+      const uint32_t x0 = (u & 1) ? xs.z : xs.x, x1 = (u & 1) ? xs.w : xs.y;
+      // (x_c, x_c) for each column: the low or the high bf16 of an x word, twice
+      const u32x4 a = {__builtin_amdgcn_perm(x0, x0, 0x01000100u), __builtin_amdgcn_perm(x0, x0, 0x03020302u),
+                       __builtin_amdgcn_perm(x1, x1, 0x01000100u), __builtin_amdgcn_perm(x1, x1, 0x03020302u)};
+#pragma unroll
+      for (int T = 0; T < kMfTiles; ++T) {
+        const u32x4 bv = {g[T][4 * u], g[T][4 * u + 1], g[T][4 * u + 2], g[T][4 * u + 3]};
+        cl[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bv), cl[T], 0, 0, 0);
       }
-      const bf16x8_t a = as_bf16x8(cur.x[s]);
-      ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bh), ch, 0, 0, 0);
-      cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), cs, 0, 0, 0);
-      cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bl), cl, 0, 0, 0);
     }
-    const float al = half_bits_to_float(cur.a), be = half_bits_to_float(cur.b);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = fmaf(be, cs[r], fmaf(al, ch[r] + cl[r], y[r]));
+    for (int T = 0; T < kMfTiles; ++T) {
+      // this block's pair sits in lane i + 16 j
+      const uint32_t ab = static_cast<uint32_t>(
+          __builtin_amdgcn_ds_bpermute(4 * (i + 16 * j), static_cast<int>(pc[T])));
+      const float al = half_bits_to_float(static_cast<uint16_t>(ab));
+      const float be = half_bits_to_float(static_cast<uint16_t>(ab >> 16));
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[T][r] = fmaf(be, cs[r], fmaf(al, cl[T][r], y[T][r]));
+      }
+    }
   };
-  // Three buffers in rotation, loads two blocks ahead.  The rotation is unrolled rather
+  // Four buffers in rotation, loads three blocks ahead.  The rotation is unrolled rather
   // than copied: a copy of a buffer whose loads are in flight would wait for them.
-  auto step = [&](const MfBlock<NMF>& cur, MfBlock<NMF>& fill, int64_t b) {
-    load(fill, b + 2 < b_last ? b + 2 : b_last);
+  // A group of four always runs all four steps (the loads stay unconditional); a block
+  // past the wave's range adds nothing.
+  auto step = [&](const MfBlock<NMF>& cur, MfBlock<NMF>& fill, int64_t b, int j) {
+    load(fill, clampb(b + 3));
     __builtin_amdgcn_sched_barrier(0);  // the later block's loads go out before this one's math
-    compute(cur);
+    compute(cur, j, b < b_end);
   };
-  for (int64_t b = b_begin; b < b_end; b += 3) {
-    step(b0, b2, b);
-    if (b + 1 < b_end) step(b1, b0, b + 1);
-    if (b + 2 < b_end) step(b2, b1, b + 2);
-  }
-  part[wave][lane] = y;
-  __syncthreads();
-  if (wave != 0) return;
-  mf32x4_t acc = part[0][lane];
+  for (int64_t b = b_begin; b < b_end; b += 4) {
 #pragma unroll
-  for (int w = 1; w < kMfWaves; ++w) {
-    const mf32x4_t v = part[w][lane];
+    for (int T = 0; T < kMfTiles; ++T) pc[T] = pn[T];
+    load_params(pn, b + 4);
+    step(b0, b3, b, 0);
+    step(b1, b0, b + 1, 1);
+    step(b2, b1, b + 2, 2);
+    step(b3, b2, b + 3, 3);
+  }
+#pragma unroll
+  for (int T = 0; T < kMfTiles; ++T) part[wave][T][lane] = y[T];
+  __syncthreads();
+  if (wave >= kMfTiles) return;
+  // wave T adds tile T's partial results in wave order
+  mf32x4_t acc = part[0][wave][lane];
+  for (int w = 1; w < NW; ++w) {
+    const mf32x4_t v = part[w][wave][lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] += v[r];
   }
-  // lane l holds tokens 4 (l / 16) + r of row l % 16
-  if (row0 + i < N) {
+  // lane l holds tokens 4 (l / 16) + r of row l % 16 of the tile
+  const int64_t orow = row0 + 16 * wave + i;
+  if (orow < N) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = 4 * h + r;
-      if (tok < d.n_tokens) d.y[int64_t(tok) * N + row0 + i] = acc[r];
+      if (tok < d.n_tokens) d.y[int64_t(tok) * N + orow] = acc[r];
     }
   }
 }
@@ -823,6 +898,18 @@ hipError_t launch_absmean(const void* x, int dtype, int64_t n_tokens, int64_t n_
   return hipGetLastError();
 }
 
+template <int NMF>
+hipError_t launch_gemv_mfma(const GemvDesc& d, int nw, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((d.n_rows + kMfRows - 1) / kMfRows));
+  if (nw == 8)
+    hipLaunchKernelGGL((gemv_mfma_kernel<NMF, 8>), grid, dim3(8 * 64), 0, stream, d);
+  else if (nw == 4)
+    hipLaunchKernelGGL((gemv_mfma_kernel<NMF, 4>), grid, dim3(4 * 64), 0, stream, d);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<NMF, 2>), grid, dim3(2 * 64), 0, stream, d);
+  return hipGetLastError();
+}
+
 int plan_gemv_split_log2(int64_t n_rows, int64_t n_cols, int rows_per_wave, int64_t target) {
   // split K over up to 4 waves of a workgroup while the grid holds fewer than `target`
   // waves and every lane keeps at least two chunks of its slice
@@ -850,16 +937,14 @@ hipError_t launch_gemv_mt(const GemvDesc& d, hipStream_t stream) {
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
   // bf16 activations and groups of whole 32-column MFMA steps go to the matrix cores
-  if (d.x_bf16 && d.group % 32 == 0 && d.n_tokens >= kGemvMfmaMinTokens && aligned(d.x, 16) &&
-      aligned(d.codes, 16)) {
-    const dim3 grid(static_cast<uint32_t>((d.n_rows + kMfRows - 1) / kMfRows));
-    if (d.group == 32)
-      hipLaunchKernelGGL((gemv_mfma_kernel<1>), grid, dim3(kMfWaves * 64), 0, stream, d);
-    else if (d.group == 64)
-      hipLaunchKernelGGL((gemv_mfma_kernel<2>), grid, dim3(kMfWaves * 64), 0, stream, d);
-    else
-      hipLaunchKernelGGL((gemv_mfma_kernel<4>), grid, dim3(kMfWaves * 64), 0, stream, d);
-    return hipGetLastError();
+  if (d.x_bf16 && d.group % 32 == 0 && d.n_tokens >= kGemvMfmaMinTokens && d.n_cols <= kMfMaxCols &&
+      aligned(d.x, 16) && aligned(d.codes, 16)) {
+    // waves per workgroup: at least 8 blocks of 128 columns per wave, at most 8 waves
+    const int64_t kb = d.n_cols / 128;
+    const int nw = kb >= 64 ? 8 : kb >= 32 ? 4 : 2;
+    if (d.group == 32) return launch_gemv_mfma<1>(d, nw, stream);
+    if (d.group == 64) return launch_gemv_mfma<2>(d, nw, stream);
+    return launch_gemv_mfma<4>(d, nw, stream);
   }
   const bool short_rows = d.n_cols <= kGvLongK;
   if (d.n_tokens <= 1)

@@ -178,7 +178,7 @@ struct GemvDesc {
 };
 constexpr int kGemvMaxTokens = 8;
 // token counts from which bf16 activations use the matrix-core kernel (measured)
-constexpr int kGemvMfmaMinTokens = 5;
+constexpr int kGemvMfmaMinTokens = 3;
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t stream);
 
 }  // namespace any4
