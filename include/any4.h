@@ -179,8 +179,8 @@ int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const
  * rule is the same as any4_quantize's, so the fixed points are too; the sums differ
  * only in fp64 rounding order.  Uses m->n_rows and m->n_cols only (other fields
  * ignored); params->group is checked but unused and the symmetric flag of
- * params->variant selects the scaled range.  Rows of at most 4096 columns
- * (ANY4_ERR_UNSUPPORTED beyond); ANY4_ERR_INVALID_ARG for a NULL pointer with
+ * params->variant selects the scaled range.  Rows of at most 16384 columns, the sorted
+ * row held in LDS (ANY4_ERR_UNSUPPORTED beyond); ANY4_ERR_INVALID_ARG for a NULL pointer with
  * n_rows > 0, n_cols < 2 or odd, or bad params.  A row holding a non-finite w_s or a
  * (which any4_stage_scale reports through its status) gives unspecified centroids for
  * that row only.  The caller owns every buffer.  Asynchronous on `stream`. */

@@ -30,6 +30,11 @@ SHAPES = [
     ("symmetric_k2048_any3", 8, 2048, BF16, 64, 8, 20, SYM, 305),
     ("unweighted_k3000_any1", 6, 3000, BF16, 8, 2, 20, W_NONE, 306),
     ("many_rounds_k512", 6, 512, BF16, 128, 16, 200, 0, 307),
+    # rows past 4096 columns (the instance with 32 compare pairs per thread): the layer's
+    # down_proj length, the longest supported row, and a ragged one
+    ("down_proj_k14336", 4, 14336, BF16, 128, 16, 20, 0, 308),
+    ("max_k16384_any3_sym", 3, 16384, BF16, 64, 8, 20, SYM, 309),
+    ("ragged_k10002_g2", 3, 10002, F32, 2, 16, 12, W_NONE, 310),
 ]
 
 
@@ -177,7 +182,7 @@ def test_sorted_lloyd_is_deterministic_and_agrees_with_the_register_path():
 
 def test_sorted_lloyd_rejects_long_rows_and_bad_shapes():
     dev = torch.device("cuda")
-    ws = torch.zeros((2, 4098), device=dev)
+    ws = torch.zeros((2, 16386), device=dev)
     c0 = torch.zeros((2, 16), device=dev)
     with pytest.raises(any4().Any4Error):
         any4().stage_lloyd_sorted(ws, ws, c0)

@@ -466,7 +466,7 @@ def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16, variant=0):
 
 def stage_lloyd_sorted(w_s, a, c_in, n_clusters=16, iters=20, variant=0, group=128):
     """Sorted-row Lloyd: ``iters`` rounds from c_in [N, n_clusters] on the scaled rows
-    w_s and sample weights a ([N, K] fp32, K <= 4096); returns c_out [N, n_clusters]."""
+    w_s and sample weights a ([N, K] fp32, K <= 16384); returns c_out [N, n_clusters]."""
     torch = _torch()
     _require_gpu(w_s)
     N, K = w_s.shape

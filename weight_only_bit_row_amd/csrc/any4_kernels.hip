@@ -74,7 +74,7 @@ __global__ void restart_merge_kernel(MergeDesc d) {
 //   [Smem][key: kp floats][a: kp floats][chunk bases: 2 x 257 fp64]
 // with kp the row length rounded up to a power of two (padding keys +inf, a 0); a
 // prefix sum inside a chunk is its base plus that chunk's elements added in order.
-// ~40 KB at 4096 columns, so three rows share a CU.
+// ~40 KB at 4096 columns, so three rows share a CU; 133 KB at 16384, one row per CU.
 constexpr int kSortedThreads = 256;
 constexpr int kSortedRegs = 16;  // consecutive elements per thread in the register steps
 
@@ -122,6 +122,8 @@ __device__ __forceinline__ void sort_small_strides(float* key, float* wt, int ti
   }
 }
 
+// PER: compare pairs per thread in an LDS step, kp / 512 for the largest kp of the instance
+template <int PER>
 __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Smem& S = *reinterpret_cast<Smem*>(smem_raw);
@@ -146,7 +148,6 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
   // LDS reads are in flight together; every index belongs to one pair per step.
   // With kSortedRegs elements per thread (kp = 4096), the steps of stride below
   // kSortedRegs stay inside a thread's consecutive elements and run in registers.
-  constexpr int PER = kSortedMaxCols / 2 / kSortedThreads;
   const int half = kp / 2;
   const bool regs = kp == kSortedThreads * kSortedRegs;
   for (int size = 2; size <= kp; size <<= 1) {
@@ -320,8 +321,17 @@ hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
   int kp = 2;
   while (kp < d.n_cols) kp <<= 1;
   d.kp = kp;
-  hipLaunchKernelGGL(sorted_lloyd_kernel, dim3(static_cast<unsigned>(d.n_rows)), dim3(kSortedThreads),
-                     sorted_lloyd_lds_bytes(d.n_cols), stream, d);
+  // rows up to 4096 columns take the instance with 8 pairs per thread (its step registers
+  // sized for them); longer rows up to kSortedMaxCols the one with 32
+  constexpr int kSmallCols = kSortedThreads * kSortedRegs;
+  static_assert(kSortedMaxCols == 4 * kSmallCols, "the large instance covers 4x the small one");
+  const dim3 grid(static_cast<unsigned>(d.n_rows));
+  if (kp <= kSmallCols)
+    hipLaunchKernelGGL((sorted_lloyd_kernel<kSmallCols / 2 / kSortedThreads>), grid, dim3(kSortedThreads),
+                       sorted_lloyd_lds_bytes(d.n_cols), stream, d);
+  else
+    hipLaunchKernelGGL((sorted_lloyd_kernel<kSortedMaxCols / 2 / kSortedThreads>), grid, dim3(kSortedThreads),
+                       sorted_lloyd_lds_bytes(d.n_cols), stream, d);
   return hipGetLastError();
 }
 

@@ -94,8 +94,9 @@ hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_
 // Sorted-row Lloyd rounds behind any4_stage_lloyd_sorted: from the scaled rows w_s and
 // sample weights a ([n_rows, n_cols] fp32 each) and the centroids c_in [n_rows, k], run
 // `iters` rounds and write c_out [n_rows, k].  One 256-lane workgroup per row, the row
-// sorted in LDS, so rows hold at most kSortedMaxCols columns.
-constexpr int kSortedMaxCols = 4096;
+// sorted in LDS (8 bytes per padded column: 128 KB at 16384), so rows hold at most
+// kSortedMaxCols columns.
+constexpr int kSortedMaxCols = 16384;
 struct SortedDesc {
   const float* w_s;
   const float* a;
