@@ -757,12 +757,32 @@ __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int 
                                                     float& sv, int& si, float& t,
                                                     uint32_t& tc) {
   float cn = sv;
-  if (lane < U) {
-    double s0 = S.wred[0][lane], s1 = S.wred[0][kMaxClusters + lane];
-    for (int w = 1; w < nw; ++w) {
-      s0 += S.wred[w][lane];
-      s1 += S.wred[w][kMaxClusters + lane];
+  double s0 = 0.0, s1 = 0.0;
+  if (nw <= 4) {
+    if (lane < U) {
+      s0 = S.wred[0][lane];
+      s1 = S.wred[0][kMaxClusters + lane];
+      for (int w = 1; w < nw; ++w) {
+        s0 += S.wred[w][lane];
+        s1 += S.wred[w][kMaxClusters + lane];
+      }
     }
+  } else {
+    // many waves: lanes p + 16 j (j < 4) add waves j, j + 4, j + 8, ... of position p, then
+    // lane p adds the four partials in j order (a fixed order, shorter than nw dependent
+    // reads); positions p >= U add what their bins hold (zeros) and are not used
+    const int p = lane & (kMaxClusters - 1), j = lane >> 4;
+    for (int w = j; w < nw; w += 4) {
+      s0 += S.wred[w][p];
+      s1 += S.wred[w][kMaxClusters + p];
+    }
+    const double a0 = __shfl(s0, p + 16), a1 = __shfl(s1, p + 16);
+    const double b0 = __shfl(s0, p + 32), b1 = __shfl(s1, p + 32);
+    const double c0 = __shfl(s0, p + 48), c1 = __shfl(s1, p + 48);
+    s0 = ((s0 + a0) + b0) + c0;
+    s1 = ((s1 + a1) + b1) + c1;
+  }
+  if (lane < U) {
     if (s0 > 0.0) cn = static_cast<float>(s1 / s0);
     S.c[si] = cn;
   }
@@ -1074,11 +1094,20 @@ void any4_rows_kernel(const LaunchArgs args) {
         if (nw > 1) {
           if (lane == kWave - 1) S.ured[t & 1][wave] = incl;
           __syncthreads();
-          Q = 0;
-          for (int w = 0; w < nw; ++w) {
-            const unsigned long long v = S.ured[t & 1][w];
-            if (w < wave) woff += v;
-            Q += v;
+          if (nw <= 4) {
+            Q = 0;
+            for (int w = 0; w < nw; ++w) {
+              const unsigned long long v = S.ured[t & 1][w];
+              if (w < wave) woff += v;
+              Q += v;
+            }
+          } else {
+            // many waves: lane w reads wave w's total and one scan gives every prefix
+            // (exact integers, so the order does not matter), instead of nw dependent reads
+            const unsigned long long v = lane < nw ? S.ured[t & 1][lane] : 0ull;
+            const unsigned long long inc = wave_incl_scan_u64(v);
+            Q = readlane_u64(inc, nw - 1);
+            woff = wave == 0 ? 0ull : readlane_u64(inc, wave - 1);
           }
         }
         const unsigned long long excl = woff + incl - ls;
