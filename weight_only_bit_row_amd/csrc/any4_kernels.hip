@@ -276,7 +276,8 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
       S.wred[0][kMaxClusters + lane] = c1;
     }
     wave_lds_fence();
-    U = update_and_structure(S, 1, k, G, off, lane, U, sv, si, t, tc);
+    bool same;
+    U = update_and_structure(S, 1, k, G, off, lane, U, sv, si, t, tc, same);
   }
   if (lane < k) d.c_out[row * k + lane] = S.c[lane];
 }

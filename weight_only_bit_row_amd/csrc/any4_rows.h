@@ -108,7 +108,8 @@ struct Smem {
   int use_table;                        // this round's cell table is complete
   int bad[kMaxWaves];                           // per-wave vote: the row holds a bad value
   float rstat[3][kMaxWaves];                    // per-wave max a, min w_S, max w_S
-  int pad_[2];
+  int done;                                     // the centroids reached a fixed point
+  int pad_[1];
 };
 
 constexpr size_t kSmemHdr = (sizeof(Smem) + 15) & ~size_t(15);
@@ -752,10 +753,12 @@ __device__ __forceinline__ void zero_bins(double* bins, int lane) {
 // strictly increasing by position, the sorted order and the lowest-index map are
 // unchanged: only the values and the switch points are recomputed, the right neighbour
 // coming from the next lane by DPP.  Otherwise the structure is rebuilt from the
-// draw-order centroids.  Returns U; (t, tc) as in build_structure.
+// draw-order centroids.  Returns U; (t, tc) as in build_structure.  `same` tells whether
+// every centroid kept its bits: then the next round's assignment, and so its sums, are
+// this round's, and every later round would give the same centroids again.
 __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int G, float off, int lane, int U,
                                                     float& sv, int& si, float& t,
-                                                    uint32_t& tc) {
+                                                    uint32_t& tc, bool& same) {
   float cn = sv;
   double s0 = 0.0, s1 = 0.0;
   if (nw <= 4) {
@@ -786,6 +789,7 @@ __device__ __forceinline__ int update_and_structure(Smem& S, int nw, int k, int 
     if (s0 > 0.0) cn = static_cast<float>(s1 / s0);
     S.c[si] = cn;
   }
+  same = __ballot(lane < U && __float_as_uint(cn) != __float_as_uint(sv)) == 0ull;
   const float cnext = dppf<0x101>(cn);  // row_shl:1, value of lane + 1 (lanes < 16)
   const bool out_of_order = lane + 1 < U && !(cn < cnext);
   if (U == k && __ballot(out_of_order) == 0ull) {
@@ -1267,10 +1271,14 @@ void any4_rows_kernel(const LaunchArgs args) {
     if (wave == 0) {
       float t;
       uint32_t tc;
-      U = update_and_structure(S, nw, k, G, cell_off, lane, U, sv, si, t, tc);
+      bool same;
+      U = update_and_structure(S, nw, k, G, cell_off, lane, U, sv, si, t, tc, same);
       build_table(S, table, lane, t, tc, U);
+      if (lane == 0) S.done = same ? 1 : 0;
     }
     __syncthreads();
+    // a fixed point: the remaining rounds would reproduce these centroids bit for bit
+    if (S.done != 0) break;
   }
   if (MODE == MODE_STEP) {
     if (tid < k) M.c_out[row * k + tid] = S.c[tid];
