@@ -157,6 +157,38 @@ def test_t4_end_to_end(case):
     say(f"  {name}: rows with identical codes {same_rows.mean():.4f}, dJ/J {(J - Jr) / max(Jr, 1e-300):.2e}")
 
 
+# Many rounds: most rows reach an exact fixed point well before the last round and the
+# kernel stops there; the oracle runs every round, so the two must still agree row by row.
+MANY_ROUNDS = [("g64_bf16_64_rounds", 40, 2048, BF16, 64, 16, 102, 64),
+               ("two_waves_k8192_48_rounds", 6, 8192, BF16, 128, 16, 40, 48),
+               ("seven_waves_k14336_40_rounds", 5, 14336, BF16, 128, 16, 42, 40),
+               ("any2_k4096_30_rounds", 8, 4096, BF16, 128, 4, 45, 30)]
+
+
+@pytest.mark.parametrize("shape", MANY_ROUNDS, ids=[s[0] for s in MANY_ROUNDS])
+def test_t4_many_rounds_fixed_point_stop(shape):
+    name, N, K, dtype, g, k, seed, iters = shape
+    say(f"T4 many rounds {name}")
+    m = make_matrix(name, N, K, dtype, seed)
+    w, act = to_device(m)
+    out, c_final, picks, ws = any4().stage_full(w, act, group=g, n_clusters=k, iters=iters, seed=0)
+    torch.cuda.synchronize()
+    assert any4().read_status(ws) == 0
+    ref = oracle.quantize(m.w, m.dtype, m.act, g, k, iters, seed=0)
+    assert np.array_equal(picks.cpu().numpy(), ref["picks"])
+    J, Jr = out.objective.cpu().numpy().sum(), ref["objective"].sum()
+    assert abs(J - Jr) <= OBJECTIVE_REL * Jr, (J, Jr)
+    same_rows = check_rows(any4(), m, g, k, iters, 0, out.codes.cpu().numpy(), c_final.cpu().numpy(),
+                           out.lut.cpu().numpy().view(np.uint16), ref, np.arange(N))
+    # one round more changes nothing on a row that reached a fixed point in both runs
+    c_more = any4().stage_full(w, act, group=g, n_clusters=k, iters=iters + 1, seed=0)[1].cpu().numpy()
+    ref_more = oracle.quantize(m.w, m.dtype, m.act, g, k, iters + 1, seed=0)
+    fixed = np.all(ref_more["c_final"].view(np.uint32) == ref["c_final"].view(np.uint32), axis=1)
+    for i in np.nonzero(fixed & same_rows)[0]:
+        assert np.array_equal(c_more[i].view(np.uint32), c_final.cpu().numpy()[i].view(np.uint32)), (name, i)
+    say(f"  {name}: rows identical {same_rows.mean():.3f}, at a fixed point {fixed.mean():.3f}")
+
+
 def test_t6_repeat_and_row_shards(case):
     name, m, g, k = case
     say(f"T6 determinism {name}")
