@@ -121,10 +121,10 @@ int main() {
   EXPECT(any4_stage_seed(&m, &p, nullptr, nullptr, nullptr), ANY4_ERR_INVALID_ARG);
   EXPECT(any4_stage_lloyd_step(&m, &p, f, static_cast<uint8_t*>(P(0xC000)), f, nullptr, nullptr), ANY4_OK);
   EXPECT(any4_stage_lloyd_sorted(&m, &p, f, f, f, f, nullptr), ANY4_OK);
-  any4_matrix m5k = mat(2, 5000);
+  any4_matrix m17k = mat(2, 16386);   // past the sorted stage's 16384 columns
   any4_params g8 = p;
   g8.group = 8;
-  EXPECT(any4_stage_lloyd_sorted(&m5k, &g8, f, f, f, f, nullptr), ANY4_ERR_UNSUPPORTED);
+  EXPECT(any4_stage_lloyd_sorted(&m17k, &g8, f, f, f, f, nullptr), ANY4_ERR_UNSUPPORTED);
   EXPECT(any4_stage_pack(&m, &p, static_cast<uint8_t*>(P(0xC000)), f, f, f, nullptr), ANY4_OK);
   EXPECT(any4_stage_full(&m, &p, f, nullptr, ws256, sizeof(ws256), nullptr), ANY4_OK);
   EXPECT(any4_stage_full(&m, &p, f, nullptr, nullptr, 0, nullptr), ANY4_ERR_WORKSPACE);
