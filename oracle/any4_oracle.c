@@ -22,9 +22,8 @@
  * printed in Section 2.4.1; for the bookends E|x| and Eq. 4 dequantization, exact
  * rational means, a worked example, exact reconstruction of exact-level rows and
  * torch's bfloat16 cast; for the method variants, exact invariances, nearest-level
- * codes, draw frequencies and restart minima).  Philox4x32-10's round constants are pinned only
- * through the shared round structure (Philox4x64-10 vs numpy) and a uniformity
- * test: its absolute stream is "parity unpinned".
+ * codes, draw frequencies and restart minima).  Philox4x32-10 is pinned against
+ * rocRAND's implementation of the same generator (its host-callable engine).
  */
 #include <math.h>
 #include <stdint.h>
@@ -48,7 +47,8 @@ int oracle_any4_version(void) { return 1; }
  * high halves xor-ed with the other two words and the round key, and from the
  * products' low halves.  The key is bumped by the two Weyl constants between
  * rounds.  The 64-bit variant (checked against numpy.random.Philox) and the
- * 32-bit variant share this structure through one macro. */
+ * 32-bit variant (checked against rocRAND's engine) share this structure through one
+ * macro. */
 
 static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
     uint64_t p = (uint64_t)a * (uint64_t)b;

@@ -49,9 +49,9 @@ def test_philox4x64_counter_words_matter():
 
 
 def test_philox4x32_uniform_and_counter_sensitive():
-    """Philox4x32-10's constants are not pinned against a reference stream (none is
-    available offline): parity unpinned for the absolute stream.  Check uniformity
-    of the 64-bit draws the seeding uses and that every word of counter/key matters."""
+    """Uniformity of the 64-bit draws the seeding uses, and every word of counter/key
+    matters (the absolute stream is pinned against rocRAND in
+    test_oracle_philox_rocrand.py)."""
     n = 20000
     u = np.array([oracle.philox4x32_10([i, 3, 1, 0], [7, 0])[0] for i in range(n)], np.float64)
     hist, _ = np.histogram(u / 2.0**32, bins=20, range=(0, 1))
