@@ -239,7 +239,12 @@ static float sqdist(float x, float c) {
  * decreases, and rounding is monotone), so every q_j stays below 2^41.  (For the random
  * initialization, whose weights are the a_j of the elements not yet drawn, B = max_j a_j
  * throughout.)  When B = 0 or Q = 0 (every weight is 0, or below 2^(e-40)) the centre is
- * copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1. */
+ * copied from w_S[0] (t = 0) or from centre 0 (t > 0) and its pick is -1.
+ * From the second draw on (k-means++ and greedy), when s = 40 - e >= 0 the sample weight
+ * is scaled by the power of two before the product instead of after it:
+ * p_j = fl(fl(a_j * 2^s) * D_j) and q_j = floor(p_j).  fl(a_j * 2^s) is exact, so this
+ * equals floor(fl(a_j * D_j) * 2^s) whenever a_j * D_j is a normal fp32 number; the two
+ * differ only for products below 2^-126 in rows whose bound is below 2^-86. */
 /* Initial centres for the initializations of Appendix C.2 (Table A4):
  *   init 0  k-means++ as described above;
  *   init 1  random: k distinct elements drawn one after another, each with probability
@@ -253,7 +258,8 @@ static float sqdist(float x, float c) {
  *           the same D^2 distribution (candidate s from Philox counter word
  *           t + 16 * restart + 65536 * s, so candidate 0 is the plain draw) and keeps the
  *           one whose potential, sum_j floor(a_j * min(D_j, (w_S_j - c)^2) * 2^(40-e))
- *           with e of this draw, is smallest (the lowest s on equal potentials).  The
+ *           with e of this draw (the weight scaled before the product, as above), is
+ *           smallest (the lowest s on equal potentials).  The
  *           potentials are integers, so they compare exactly.
  * `restart` selects an independent draw stream for restarts: the Philox counter's
  * second word is t + 16 * restart. */
@@ -306,25 +312,33 @@ int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
     }
     float B = a_max;
     for (int32_t t = 0; t < k; ++t) {
-        for (int64_t j = 0; j < K; ++j) {
-            if (init == 1)
-                p[j] = (t == 0) ? a[j] : p[j];    /* drawn elements were set to 0 below */
-            else
-                p[j] = (t == 0) ? a[j] : a[j] * D[j];
-        }
         if (t == 1 && init != 1) {
             const float up = x_max - c0[0], down = c0[0] - x_min;
             const float m = up > down ? up : down;
             B = a_max * (m * m);
         }
-        uint64_t Q = 0;
         int e = 0;
         if (B > 0.0f) {
             int E;
             frexp((double)B, &E);               /* B = f * 2^E, f in [0.5, 1) */
             e = E - 1;                           /* floor(log2 B) */
+        }
+        /* the weights scaled by 2^s before the product (see above) */
+        const int prescaled = (t > 0 && init != 1 && 40 - e >= 0);
+        for (int64_t j = 0; j < K; ++j) {
+            if (init == 1)
+                p[j] = (t == 0) ? a[j] : p[j];    /* drawn elements were set to 0 below */
+            else if (t == 0)
+                p[j] = a[j];
+            else if (prescaled)
+                p[j] = ldexpf(a[j], 40 - e) * D[j];
+            else
+                p[j] = a[j] * D[j];
+        }
+        uint64_t Q = 0;
+        if (B > 0.0f) {
             for (int64_t j = 0; j < K; ++j) {
-                double v = ldexp((double)p[j], 40 - e);
+                double v = prescaled ? (double)p[j] : ldexp((double)p[j], 40 - e);
                 q[j] = (uint64_t)floor(v);
                 Q += q[j];
             }
@@ -353,7 +367,8 @@ int oracle_seed_row_init(const float* ws, const float* a, int64_t K, int32_t k,
                     for (int64_t j = 0; j < K; ++j) {
                         float d = sqdist(ws[j], ws[cand]);
                         float m = d < D[j] ? d : D[j];
-                        pot += (uint64_t)floor((double)(a[j] * m) * sc);
+                        pot += prescaled ? (uint64_t)floor((double)(ldexpf(a[j], 40 - e) * m))
+                                         : (uint64_t)floor((double)(a[j] * m) * sc);
                     }
                     if (s == 0 || pot < best_pot) {
                         best_pot = pot;

@@ -318,6 +318,27 @@ def test_seed_scale_is_fixed_after_the_first_pick():
         assert np.all(picks[2:] == -1)        # after 15 is drawn every D is 0: copies
 
 
+def test_seed_picks_invariant_under_power_of_two_weights():
+    """D^2 sampling is scale-free in the weights, and the integer CDF keeps it so down to
+    the bottom of fp32: from the second draw on, a_j is scaled by 2^(40-e) before its
+    product with D_j.  A row whose weights are another's times 2^-123 (still normal
+    numbers) draws the same picks, although the products a_j * D_j of its tight cluster
+    lie near 2^-146, where fp32 keeps 2-3 bits: rounding those products first would move
+    their terms q_j (around 2^10) by up to a fifth and change the picks."""
+    rng = np.random.default_rng(31)
+    x = np.concatenate([[0.0, 15.0], 7.0 + rng.uniform(0, 7e-4, 46)]).astype(np.float32)
+    a = rng.uniform(0.5, 1.0, x.size).astype(np.float32)       # full 24-bit mantissas
+    a_tiny = (a * np.float32(2.0 ** -123)).astype(np.float32)  # exact: still normal numbers
+    assert np.array_equal((a_tiny.astype(np.float64) * 2.0 ** 123).astype(np.float32), a)
+    inside = 0
+    for seed in range(300):
+        p1 = oracle.seed_row(x, a, 8, seed=seed)[1]
+        p2 = oracle.seed_row(x, a_tiny, 8, seed=seed)[1]
+        assert np.array_equal(p1, p2), (seed, p1, p2)
+        inside += int(np.sum(p1[1:] >= 2))  # later picks inside the tight cluster
+    assert inside > 900  # the draws do reach the elements whose products are subnormal
+
+
 def test_seed_depends_on_row_matrix_and_key():
     rng = np.random.default_rng(12)
     x = rng.uniform(0, 15, 256).astype(np.float32)
