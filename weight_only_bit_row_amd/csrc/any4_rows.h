@@ -94,15 +94,11 @@ struct Smem {
   };
   float fred[2][kMaxWaves];                     // per-wave fp32 partials (double buffered)
   double dred[kMaxWaves];                       // per-wave fp64 partials
-  unsigned long long ured[2][kMaxWaves];        // per-wave u64 partials (double buffered)
+  alignas(16) unsigned long long ured[2][kMaxWaves];  // per-wave u64 partials (double buffered)
   unsigned long long u[kMaxClusters];   // Philox draw of each seeding step
-  alignas(16) float stage_p[kWave];     // sampling weights of the lane owning a pick
-  alignas(16) float stage_x[kWave];     // its scaled values
   int picks[kMaxClusters];
-  unsigned long long owner_excl;
   float x0;                             // w_S of column 0
   float pick_c;
-  int owner;
   int pick_j;
   int n_unique;
   int use_table;                        // this round's cell table is complete
@@ -166,9 +162,10 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Wave-level reductions and scans with DPP lane moves (VALU latency, no LDS round
 // trip).  Controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror
 // 0x141, row_mirror 0x140, row_shr:n 0x110+n, row_bcast:15 0x142, row_bcast:31 0x143.
+// Lanes without a source lane (row shifts) read 0; rows outside ROW_MASK keep 0.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, ROW_MASK == 0xF);
 }
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dppf(float v) {
@@ -233,13 +230,15 @@ __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long l
   v += dpp64<0x143, 0xC>(v);
   return v;
 }
-__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+// inclusive prefix sums over lanes 0..N-1 (N <= 32; lanes past N hold partial sums)
+template <int N>
+__device__ __forceinline__ double lanes_incl_scan_f64(double v) {
+  static_assert(N <= 32, "two DPP rows at most");
   v += dppd<0x111>(v);
   v += dppd<0x112>(v);
-  v += dppd<0x114>(v);
-  v += dppd<0x118>(v);
-  v += dppd<0x142, 0xA>(v);
-  v += dppd<0x143, 0xC>(v);
+  if constexpr (N > 4) v += dppd<0x114>(v);
+  if constexpr (N > 8) v += dppd<0x118>(v);
+  if constexpr (N > 16) v += dppd<0x142, 0xA>(v);
   return v;
 }
 
@@ -613,14 +612,27 @@ __device__ __forceinline__ void scale_wide(float (&x)[E], float (&act)[E], const
 }
 
 // ---------------------------------------------------------------------------------
+// Lane l's x[m] for a wave-uniform m and l: a binary search over m (uniform branches)
+// ending in one readlane, so no vector register holds a copy of x.
+template <int LO, int N, int E>
+__device__ __forceinline__ float readlane_elem(const float (&x)[E], int m, int l) {
+  if constexpr (N == 1) {
+    return readlane_f(x[LO], l);
+  } else {
+    if (m < LO + N / 2) return readlane_elem<LO, N / 2, E>(x, m, l);
+    return readlane_elem<LO + N / 2, N - N / 2, E>(x, m, l);
+  }
+}
+
 // The k-means++ sampling weights of a lane's E elements: in registers, or, for rows of
 // 5-16 waves (1024-lane workgroups, 128 VGPRs, where they would spill), in the wave's
 // bin area, which seeding does not use (element m of lane l at word m * 64 + l, so a
-// wave's accesses to one m hit 64 consecutive words).
+// wave's accesses to one m hit 64 consecutive words).  Register-held weights are copied
+// to that layout with every CDF pass, where the owner of a pick reads them.
 template <int E, bool IN_LDS>
 struct SeedWeights {
   float r[IN_LDS ? 1 : E];
-  float* l;
+  float* l;  // this lane's weight m at l[m * kWave]
   __device__ __forceinline__ float& operator[](int m) {
     if constexpr (IN_LDS)
       return l[m * kWave];
@@ -1003,16 +1015,22 @@ void any4_rows_kernel(const LaunchArgs args) {
       philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
       S.gk.u[s - 1][t] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
     }
+    // The sampling weights of every draw are in the wave's bin area (which seeding does
+    // not use) when the owner of a pick looks for its element: rows of 5-16 waves keep
+    // them there, the others keep them in registers and copy them there with each CDF pass.
     constexpr bool kPvLds = NWMAX > 8;
-    static_assert(!kPvLds || E * kWave * sizeof(float) <= kBinBytesPerWave, "weights fit the bins");
+    static_assert(E * kWave * sizeof(float) <= kBinBytesPerWave, "weights fit the bins");
+    float* const pv_area = reinterpret_cast<float*>(smem_raw + kSmemHdr + kTableBytes + wave * kBinBytesPerWave);
     SeedWeights<E, kPvLds> pv;
-    pv.l = reinterpret_cast<float*>(smem_raw + kSmemHdr + kTableBytes + wave * kBinBytesPerWave) + lane;
-#pragma unroll
-    for (int m = 0; m < E; ++m) pv[m] = av[m];
+    pv.l = pv_area + lane;
     // Integer CDF terms floor(p * 2^ksc), ksc = 40 - floor(log2 B), for a bound B of the
     // draw's weights: the largest sample weight for the first draw, and one bound for all
     // later draws, fixed after the first pick (below).  B = 0 leaves every term 0 and the
-    // centre is copied.
+    // centre is copied.  The weights are held scaled, pv = p * 2^ksc, so a term is
+    // floor(pv): the scale is exact (pv < 2^41; a value that underflows is below 1 and
+    // floors to 0 either way), and so is the floor.  From the second k-means++ draw on,
+    // with ksc >= 0, the sample weights themselves carry the scale (a' = a * 2^ksc, exact,
+    // undone after seeding) and pv = fl(a' * D); with ksc < 0, pv = fl(fl(a * D) * 2^ksc).
     int ksc = 0;
     bool live = a_max > 0.0f;
     if (live) {
@@ -1020,10 +1038,15 @@ void any4_rows_kernel(const LaunchArgs args) {
       frexpf(a_max, &e2);
       ksc = 40 - (e2 - 1);
     }
+#pragma unroll
+    for (int m = 0; m < E; ++m) pv[m] = ldexpf(av[m], ksc);
+    bool pre = false;  // av holds a * 2^ksc
     __syncthreads();
+    const unsigned long long u_lane = S.u[lane & (kMaxClusters - 1)];  // draw t's Philox output in lane t
     float ct = 0.0f, c_first = 0.0f;  // the previous centre and centre 0 (uniform)
     int pick = -1;
     for (int t = 0; t < k; ++t) {
+      __builtin_amdgcn_s_setprio(0);
       if (t == 1 && init != INIT_RANDOM) {
         // no later weight a_j * D_j exceeds max_j a_j * m^2, m the larger distance from
         // centre 0 to the row's extremes (D only decreases; rounding is monotone)
@@ -1041,15 +1064,18 @@ void any4_rows_kernel(const LaunchArgs args) {
           frexpf(bound, &e2);
           ksc = 40 - (e2 - 1);
         }
+        pre = __builtin_amdgcn_readfirstlane((live && ksc >= 0) ? 1 : 0) != 0;
+        const int ka = pre ? ksc : 0;
+#pragma unroll
+        for (int m = 0; m < E; ++m) av[m] = ldexpf(av[m], ka);
       }
-      // This draw's sampling weights, then their CDF terms.  For t >= 1 the weights are
-      // a_j * min_t fl((w_S_j - c_t)^2), updated from the previous centre.
+      // This draw's scaled sampling weights, then their CDF terms.  For t >= 1 the weights
+      // are a_j * min_t fl((w_S_j - c_t)^2), updated from the previous centre (the min of
+      // the products is the product of the min: rounding is monotone).
       // They are never NaN and never below zero (a zero may be -0), so the float order is
       // the order of their bit patterns as signed integers: the min runs as an integer op,
-      // which needs no NaN quieting of its operands.  Each term floor(p * 2^ksc) is taken
-      // in fp32: the power-of-two scale is exact (p * 2^ksc < 2^41; a result that
-      // underflows is below 1 and floors to 0 either way) and so is the floor, then
-      // widened to fp64 exactly (a lane's sum stays below 2^46).
+      // which needs no NaN quieting of its operands.  Each term floor(pv) is widened to
+      // fp64 exactly (a lane's sum stays below 2^46).
       if (t > 0 && init == INIT_RANDOM) {
         // random initialization (Appendix C.2): the drawn element leaves the pool, the
         // others keep their weight a_j
@@ -1058,19 +1084,38 @@ void any4_rows_kernel(const LaunchArgs args) {
         for (int m = 0; m < E; ++m)
           if (m == pm) pv[m] = 0.0f;
       } else if (t == 1) {
+        if (pre) {
 #pragma unroll
-        for (int m = 0; m < E; ++m) {
-          float d = xv[m] - ct;
-          d = d * d;
-          pv[m] = av[m] * d;
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            pv[m] = av[m] * d;
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            pv[m] = ldexpf(av[m] * d, ksc);
+          }
         }
       } else if (t > 1 && !kPvLds) {
+        if (pre) {
 #pragma unroll
-        for (int m = 0; m < E; ++m) {
-          float d = xv[m] - ct;
-          d = d * d;
-          const int pd = __float_as_int(av[m] * d);
-          pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            const int pd = __float_as_int(av[m] * d);
+            pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            const int pd = __float_as_int(ldexpf(av[m] * d, ksc));
+            pv[m] = __int_as_float(min(__float_as_int(pv[m]), pd));
+          }
         }
       }
       double lsum = 0.0;
@@ -1078,20 +1123,39 @@ void any4_rows_kernel(const LaunchArgs args) {
         // weights in LDS: the update and the CDF term in one pass, one read and one
         // write of each weight (in registers the two passes stay apart, which keeps the
         // register pressure of the fused pass off the seeding loop)
+        if (pre) {
 #pragma unroll
-        for (int m = 0; m < E; ++m) {
-          float d = xv[m] - ct;
-          d = d * d;
-          const int pd = __float_as_int(av[m] * d);
-          const float p = __int_as_float(min(__float_as_int(pv[m]), pd));
-          pv[m] = p;
-          lsum += static_cast<double>(floorf(ldexpf(p, ksc)));
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            const int pd = __float_as_int(av[m] * d);
+            const float p = __int_as_float(min(__float_as_int(pv[m]), pd));
+            pv[m] = p;
+            lsum += static_cast<double>(floorf(p));
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < E; ++m) {
+            float d = xv[m] - ct;
+            d = d * d;
+            const int pd = __float_as_int(ldexpf(av[m] * d, ksc));
+            const float p = __int_as_float(min(__float_as_int(pv[m]), pd));
+            pv[m] = p;
+            lsum += static_cast<double>(floorf(p));
+          }
         }
       } else {
 #pragma unroll
-        for (int m = 0; m < E; ++m) lsum += static_cast<double>(floorf(ldexpf(pv[m], ksc)));
+        for (int m = 0; m < E; ++m) {
+          lsum += static_cast<double>(floorf(pv[m]));
+          if constexpr (!kPvLds) pv.l[m * kWave] = pv[m];
+        }
       }
       if (!live) lsum = 0.0;
+      // From here to the next draw's update the row runs a serial chain (exchange, pick
+      // search, broadcast) while the other rows on the SIMD run their element passes: a
+      // raised wave priority lets the chain issue first.
+      __builtin_amdgcn_s_setprio(2);
         const unsigned long long ls = static_cast<unsigned long long>(lsum);
         const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
@@ -1099,9 +1163,14 @@ void any4_rows_kernel(const LaunchArgs args) {
           if (lane == kWave - 1) S.ured[t & 1][wave] = incl;
           __syncthreads();
           if (nw <= 4) {
+            // the four slots read at once (slots past nw hold stale values and are dropped)
+            const ulonglong2 v01 = reinterpret_cast<const ulonglong2*>(S.ured[t & 1])[0];
+            const ulonglong2 v23 = reinterpret_cast<const ulonglong2*>(S.ured[t & 1])[1];
+            const unsigned long long v4[4] = {v01.x, v01.y, v23.x, v23.y};
             Q = 0;
-            for (int w = 0; w < nw; ++w) {
-              const unsigned long long v = S.ured[t & 1][w];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const unsigned long long v = w < nw ? v4[w] : 0ull;
               if (w < wave) woff += v;
               Q += v;
             }
@@ -1125,37 +1194,31 @@ void any4_rows_kernel(const LaunchArgs args) {
         // draw is candidate 0
         const int n_cand = (init == INIT_GREEDY && t > 0) ? greedy_trials(k) : 1;
         for (int s = 0; s < n_cand; ++s) {
-          const unsigned long long r = __umul64hi(s == 0 ? S.u[t] : S.gk.u[s - 1][t], Q);
+          const unsigned long long r = __umul64hi(s == 0 ? readlane_u64(u_lane, t) : S.gk.u[s - 1][t], Q);
           const bool own = ls > 0 && excl <= r && r - excl < ls;
-          // the owner's wave finds the element: the owner lane stages its weights and
-          // values, and lane m of that wave takes element m (one wave, so no block barrier)
-          if (__ballot(own) != 0ull) {
-            if (own) {
-              S.owner = tid;
-              S.owner_excl = excl;
-#pragma unroll
-              for (int v = 0; v < E / 4; ++v) {
-                reinterpret_cast<float4*>(S.stage_p)[v] =
-                    make_float4(pv[4 * v], pv[4 * v + 1], pv[4 * v + 2], pv[4 * v + 3]);
-                reinterpret_cast<float4*>(S.stage_x)[v] =
-                    make_float4(xv[4 * v], xv[4 * v + 1], xv[4 * v + 2], xv[4 * v + 3]);
-              }
-            }
-            wave_lds_fence();
-            const unsigned long long oex = S.owner_excl;
-            const double q = (lane < E) ? static_cast<double>(floorf(ldexpf(S.stage_p[lane], ksc))) : 0.0;
-            const double qi = wave_incl_scan_f64(q);
-            const bool hit = lane < E && oex + static_cast<unsigned long long>(qi) > r;
-            const unsigned long long bal = __ballot(hit);
-            int ms = __ffsll(static_cast<long long>(bal)) - 1;
+          // The owner's wave finds the element: lane m < E reads the owner lane's weight m
+          // from the bin area and the first prefix past r - excl (the draw's offset inside
+          // the owner's interval) marks it; the owner lane publishes its value.
+          const unsigned long long bal = __ballot(own);
+          if (bal != 0ull) {
+            const int ol = __ffsll(static_cast<long long>(bal)) - 1;
+            const unsigned long long rr = readlane_u64(r - excl, ol);
+            wave_lds_fence();  // a one-wave row reads its own copies without a barrier
+            const double q = (lane < E) ? static_cast<double>(floorf(pv_area[lane * kWave + ol])) : 0.0;
+            const double qi = lanes_incl_scan_f64<E>(q);
+            const bool hit = lane < E && qi > static_cast<double>(rr);  // exact integers below 2^47
+            int ms = __ffsll(static_cast<long long>(__ballot(hit))) - 1;
             if (ms < 0) ms = E - 1;  // unreachable: the owner's prefix always crosses r
+            ms = __builtin_amdgcn_readfirstlane(ms);
+            const float xm = readlane_elem<0, E, E>(xv, ms, ol);
             if (lane == 0) {
+              const int j = (wave * kWave + ol) * E + ms;
               if (s == 0) {
-                S.pick_c = S.stage_x[ms];
-                S.pick_j = S.owner * E + ms;
+                S.pick_c = xm;
+                S.pick_j = j;
               } else {
-                S.gk.cand_c[s] = S.stage_x[ms];
-                S.gk.cand_j[s] = S.owner * E + ms;
+                S.gk.cand_c[s] = xm;
+                S.gk.cand_j[s] = j;
               }
             }
           }
@@ -1164,8 +1227,10 @@ void any4_rows_kernel(const LaunchArgs args) {
         ct = uniform_f(S.pick_c);
         pick = __builtin_amdgcn_readfirstlane(S.pick_j);
         if (n_cand > 1) {
-          // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * 2^ksc): exact
-          // integers (per lane below 2^47 in fp64, per row in u64), compared exactly
+          // each candidate's potential sum_j floor(min(p_j, a_j (w_S_j - c)^2) * 2^ksc) (the
+          // weights scaled as above): exact integers (per lane below 2^47 in fp64, per row in
+          // u64), compared exactly
+          const int kpost = pre ? 0 : ksc;  // the scale still to apply to a product
           for (int s = 0; s < n_cand; ++s) {
             const float cs = s == 0 ? ct : S.gk.cand_c[s];
             double lp = 0.0;
@@ -1173,8 +1238,9 @@ void any4_rows_kernel(const LaunchArgs args) {
             for (int m = 0; m < E; ++m) {
               float d = xv[m] - cs;
               d = d * d;
-              const int pm = min(__float_as_int(pv[m]), __float_as_int(av[m] * d));
-              lp += static_cast<double>(floorf(ldexpf(__int_as_float(pm), ksc)));
+              const float pc = ldexpf(av[m] * d, kpost);
+              const int pm = min(__float_as_int(pv[m]), __float_as_int(pc));
+              lp += static_cast<double>(floorf(__int_as_float(pm)));
             }
             const unsigned long long tot =
                 readlane_u64(wave_incl_scan_u64(static_cast<unsigned long long>(lp)), kWave - 1);
@@ -1201,6 +1267,13 @@ void any4_rows_kernel(const LaunchArgs args) {
         S.picks[t] = pick;
       }
       if (t == 0) c_first = ct;
+    }
+    __builtin_amdgcn_s_setprio(0);
+    {
+      // back to the sample weights of Eq. 23 (exact: the scale only raised the exponents)
+      const int ka = pre ? -ksc : 0;
+#pragma unroll
+      for (int m = 0; m < E; ++m) av[m] = ldexpf(av[m], ka);
     }
     __syncthreads();
     if (MODE == MODE_SEED) {
@@ -1262,6 +1335,9 @@ void any4_rows_kernel(const LaunchArgs args) {
       else
         element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
     }
+    // the bin reduction and wave 0's centroid update are the round's serial chain: raised
+    // priority, as in seeding, until the round's second barrier
+    __builtin_amdgcn_s_setprio(2);
     // the reduction reads bins that other lanes of this wave just added to
     wave_lds_fence();
     const double total = reduce_bins(bins, lane);
@@ -1277,6 +1353,7 @@ void any4_rows_kernel(const LaunchArgs args) {
       if (lane == 0) S.done = same ? 1 : 0;
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     // a fixed point: the remaining rounds would reproduce these centroids bit for bit
     if (S.done != 0) break;
   }
@@ -1333,7 +1410,7 @@ void launch_kernel(const LaunchArgs& args, dim3 grid, dim3 block, size_t smem, h
 template <int E, int NWMAX>
 hipError_t launch_mode(const LaunchArgs& args, int mode, int64_t n_blocks, hipStream_t stream) {
   const int nw = (NWMAX == 1) ? 1 : args.nw;
-  // the bin area also holds the sampling weights of 9-16-wave rows while they seed
+  // the bin area also holds the sampling weights of 5-16-wave rows while they seed
   const size_t smem = kSmemHdr + ((mode == MODE_FULL || mode == MODE_STEP || mode == MODE_SEED)
                                       ? kTableBytes + static_cast<size_t>(nw) * kBinBytesPerWave
                                       : 0);
