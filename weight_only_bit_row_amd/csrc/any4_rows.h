@@ -513,8 +513,10 @@ __device__ __forceinline__ void finish_group(float mn, float mx, const ScalePara
       const float diff = x[m] - beta;
       ws = RECIP ? static_cast<float>(static_cast<double>(diff) * rinv) : diff / alpha;
     }
+    // x and E|x| are finite (checked on load) and so is alpha (checked above), so a is
+    // never NaN, w_S is bounded and a * w_S is finite unless a is huge: the row's
+    // largest a is checked against kAMax once, after the row vote
     const float a = (wmode == 0) ? alpha * act[m] : (wmode == 1 ? act[m] : 1.0f);
-    if (!is_finite(a) || a > kAMax || !is_finite(a * ws)) bad = true;
     x[m] = ws;
     act[m] = a;
   }
@@ -891,12 +893,14 @@ void any4_rows_kernel(const LaunchArgs args) {
   load_row<E>(M, row, K, col0, xv, av);
 
   bool bad = false;
+  if (n_valid == E) {
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    if (m < n_valid) {
-      if (!is_finite(xv[m])) bad = true;
-      if (!(av[m] >= 0.0f) || !is_finite(av[m])) bad = true;
-    }
+    for (int m = 0; m < E; ++m)
+      if (!is_finite(xv[m]) || !(av[m] >= 0.0f && av[m] <= __FLT_MAX__)) bad = true;
+  } else {
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      if (m < n_valid && (!is_finite(xv[m]) || !(av[m] >= 0.0f && av[m] <= __FLT_MAX__))) bad = true;
   }
 
   // ---- Eq. 1-2 scaling and Eq. 23 sample weights
@@ -930,12 +934,21 @@ void any4_rows_kernel(const LaunchArgs args) {
   // scaled weights, which set the k-means++ sampling scales.
   if (tid == 0) S.x0 = xv[0];
   float l_amax = 0.0f, l_xmin = __builtin_huge_valf(), l_xmax = -__builtin_huge_valf();
+  if (n_valid == E) {
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    if (m < n_valid) {
+    for (int m = 0; m < E; ++m) {
       l_amax = fmaxf(l_amax, av[m]);
       l_xmin = fminf(l_xmin, xv[m]);
       l_xmax = fmaxf(l_xmax, xv[m]);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      if (m < n_valid) {
+        l_amax = fmaxf(l_amax, av[m]);
+        l_xmin = fminf(l_xmin, xv[m]);
+        l_xmax = fmaxf(l_xmax, xv[m]);
+      }
     }
   }
   l_amax = wave_max(l_amax);
@@ -956,6 +969,7 @@ void any4_rows_kernel(const LaunchArgs args) {
     a_max = fmaxf(a_max, S.rstat[0][w]);
   }
   a_max = uniform_f(a_max);
+  row_bad = row_bad || !(a_max <= kAMax);  // a sample weight above 2^64 (or an overflow to inf)
   if (row_bad) {
     if (MODE == MODE_FULL) {
       for (int m = 0; m < E; m += 2)
