@@ -13,11 +13,13 @@
 // Each lane owns E contiguous columns of the row; the row stays in VGPRs from the
 // single HBM read to the single store of codes/LUT/scale/offset.
 //
-//   scale      group min/max in registers (shuffles for groups wider than a lane),
-//              w_S = (w - beta) / alpha with IEEE division
-//   seed       k-means++: sampling weights p_j updated in registers, exact integer
-//              CDF (fp64 per-lane sums of floor(p_j 2^(40-e)), u64 scan across lanes),
-//              Philox4x32-10 draw per (row, step)
+//   scale      group min/max in registers (DPP moves for groups wider than a lane),
+//              w_S = (w - beta) / alpha correctly rounded (IEEE division, or one fp64
+//              reciprocal per group where a lane holds one group)
+//   seed       k-means++: sampling weights p_j held scaled by 2^(40-e), in registers
+//              (in the bin area for rows of 5-16 waves), exact integer CDF (fp64 per-lane
+//              sums of floor(p_j 2^(40-e)), u64 scan across lanes), one Philox4x32-10
+//              draw per (row, step); the serial chain of each draw at raised priority
 //   Lloyd      per round: sort the <=16 centroids, merge equal values (lowest draw
 //              index kept), compute the exact fp32 switch point between each pair of
 //              sorted neighbours, and tabulate them over 2k fixed cells, each half a
