@@ -670,11 +670,9 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
                                                uint8_t* assign_row, uint32_t (&packed)[E / 8],
                                                int n_valid, int tok) {
 #ifndef ANY4_CHUNK
-#define ANY4_CHUNK 4
+#define ANY4_CHUNK 8
 #endif
-  // elements whose table reads are in flight together; the final pass takes 8, which
-  // leaves it fewer registers to spill than chunks of 4
-  constexpr int CH = KIND == PASS_FINAL ? 8 : ANY4_CHUNK;
+  constexpr int CH = ANY4_CHUNK;  // elements whose table reads are in flight together
   const float t7 = uniform_f(S.thr[7]);
   const uint32_t tbase = lds_address(const_cast<unsigned char*>(table));
   double J = 0.0;
