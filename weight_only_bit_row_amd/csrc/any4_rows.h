@@ -193,6 +193,12 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
+// A double holding an exact integer in [0, 2^52) as u64: adding 2^52 is exact and leaves
+// the integer in the mantissa bits (two ops instead of a general conversion).
+__device__ __forceinline__ unsigned long long exact_u64(double v) {
+  return static_cast<unsigned long long>(__double_as_longlong(v + 4503599627370496.0)) -
+         0x4330000000000000ull;
+}
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
@@ -966,7 +972,15 @@ void any4_rows_kernel(const LaunchArgs args) {
   __syncthreads();
   bool row_bad = false;
   float a_max = 0.0f;
-  for (int w = 0; w < nw; ++w) {
+  // the first four waves' slots read at once (slots past nw are stale and dropped)
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int bw = S.bad[w];
+    const float aw = S.rstat[0][w];
+    row_bad = row_bad || (w < nw && bw != 0);
+    a_max = fmaxf(a_max, w < nw ? aw : 0.0f);
+  }
+  for (int w = 4; w < nw; ++w) {
     row_bad = row_bad || S.bad[w] != 0;
     a_max = fmaxf(a_max, S.rstat[0][w]);
   }
@@ -1067,7 +1081,13 @@ void any4_rows_kernel(const LaunchArgs args) {
         // no later weight a_j * D_j exceeds max_j a_j * m^2, m the larger distance from
         // centre 0 to the row's extremes (D only decreases; rounding is monotone)
         float x_min = S.rstat[1][0], x_max = S.rstat[2][0];
-        for (int w = 1; w < nw; ++w) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const float lo = S.rstat[1][w], hi = S.rstat[2][w];
+          x_min = fminf(x_min, w < nw ? lo : x_min);
+          x_max = fmaxf(x_max, w < nw ? hi : x_max);
+        }
+        for (int w = 4; w < nw; ++w) {
           x_min = fminf(x_min, S.rstat[1][w]);
           x_max = fmaxf(x_max, S.rstat[2][w]);
         }
@@ -1172,7 +1192,7 @@ void any4_rows_kernel(const LaunchArgs args) {
       // search, broadcast) while the other rows on the SIMD run their element passes: a
       // raised wave priority lets the chain issue first.
       __builtin_amdgcn_s_setprio(2);
-        const unsigned long long ls = static_cast<unsigned long long>(lsum);
+        const unsigned long long ls = exact_u64(lsum);  // below 2^46
         const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long woff = 0, Q = readlane_u64(incl, kWave - 1);
         if (nw > 1) {
@@ -1259,7 +1279,7 @@ void any4_rows_kernel(const LaunchArgs args) {
               lp += static_cast<double>(floorf(__int_as_float(pm)));
             }
             const unsigned long long tot =
-                readlane_u64(wave_incl_scan_u64(static_cast<unsigned long long>(lp)), kWave - 1);
+                readlane_u64(wave_incl_scan_u64(exact_u64(lp)), kWave - 1);
             if (lane == 0) S.gk.pot[wave][s] = tot;
           }
           __syncthreads();
