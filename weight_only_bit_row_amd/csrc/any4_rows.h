@@ -428,11 +428,45 @@ __device__ __forceinline__ int sorted_position(float x, float t7, const float* t
 
 // ---------------------------------------------------------------------------------
 // Row loading: lane owns columns [col0, col0 + E); missing columns read as 0.
-template <int E>
+// `in_flight` runs while the loads are outstanding: with OVERLAP, in the common case (a
+// full lane of 16-byte aligned bf16 data) every load of W and E|x| is issued first, then
+// `in_flight`, then the conversions, so no load waits for another; otherwise (and in the
+// 128-VGPR instances, where the raw words would spill) it runs after the loads.
+template <int E, bool OVERLAP, typename F>
 __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, int col0,
-                                         float (&x)[E], float (&act)[E]) {
+                                         float (&x)[E], float (&act)[E], F&& in_flight) {
   const bool full = col0 + E <= K;
   const int nv = K - col0;  // valid columns of this lane (may be <= 0 or >= E)
+  const bool act_vec = full && (K & 3) == 0 && ((reinterpret_cast<uintptr_t>(M.act) & 15) == 0);
+  if (OVERLAP && M.dtype == 1 && act_vec && (K & 7) == 0 &&
+      ((reinterpret_cast<uintptr_t>(M.w) & 15) == 0)) {
+    const uint4* wsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(M.w) + row * (int64_t)K + col0);
+    const float4* asrc = reinterpret_cast<const float4*>(M.act + col0);
+    uint4 wr[E / 8];
+    float4 ar[E / 4];
+#pragma unroll
+    for (int v = 0; v < E / 8; ++v) wr[v] = wsrc[v];
+#pragma unroll
+    for (int v = 0; v < E / 4; ++v) ar[v] = asrc[v];
+    in_flight();
+#pragma unroll
+    for (int v = 0; v < E / 8; ++v) {
+      const uint32_t w4[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[8 * v + 2 * h] = bf16_bits_to_float(w4[h] & 0xFFFFu);
+        x[8 * v + 2 * h + 1] = bf16_bits_to_float(w4[h] >> 16);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < E / 4; ++v) {
+      act[4 * v] = ar[v].x;
+      act[4 * v + 1] = ar[v].y;
+      act[4 * v + 2] = ar[v].z;
+      act[4 * v + 3] = ar[v].w;
+    }
+    return;
+  }
   if (M.dtype == 1) {
     const uint16_t* src = static_cast<const uint16_t*>(M.w) + row * (int64_t)K + col0;
     if (full && (K & 7) == 0 && ((reinterpret_cast<uintptr_t>(M.w) & 15) == 0)) {
@@ -467,7 +501,7 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
     }
   }
   const float* asrc = M.act + col0;
-  if (full && (K & 3) == 0 && ((reinterpret_cast<uintptr_t>(M.act) & 15) == 0)) {
+  if (act_vec) {
 #pragma unroll
     for (int v = 0; v < E / 4; ++v) {
       const float4 d = reinterpret_cast<const float4*>(asrc)[v];
@@ -480,6 +514,7 @@ __device__ __forceinline__ void load_row(const MatDesc& M, int64_t row, int K, i
 #pragma unroll
     for (int m = 0; m < E; ++m) act[m] = (m < nv) ? asrc[m] : 0.0f;
   }
+  in_flight();
 }
 
 // Scaling of a call: Qmax - Qmin = qr = 2^n - 1 (Eq. 2), Qmax = qmax = 2^(n-1) for the
@@ -898,7 +933,17 @@ void any4_rows_kernel(const LaunchArgs args) {
 
   const int n_valid = (K - col0 < E) ? (K - col0 > 0 ? K - col0 : 0) : E;  // valid columns here
   float xv[E], av[E];
-  load_row<E>(M, row, K, col0, xv, av);
+  // the k-means++ draws, one Philox4x32-10 block per (row, step), computed while the row
+  // loads (restart r uses the counters t + 16 r); read after the row vote's barrier
+  load_row<E, (NWMAX <= 8)>(M, row, K, col0, xv, av, [&]() {
+    if ((MODE == MODE_FULL || MODE == MODE_SEED) && init != INIT_UNIFORM && tid < k) {
+      const uint64_t rid = static_cast<uint64_t>(M.row_offset + row);
+      uint32_t c[4] = {static_cast<uint32_t>(rid), static_cast<uint32_t>(tid + 16 * restart),
+                       static_cast<uint32_t>(M.matrix_index), static_cast<uint32_t>(rid >> 32)};
+      philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
+      S.u[tid] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
+    }
+  });
 
   bool bad = false;
   if (n_valid == E) {
@@ -1027,14 +1072,6 @@ void any4_rows_kernel(const LaunchArgs args) {
     }
     if (M.picks_out && tid < k) M.picks_out[row * k + tid] = -1;
   } else {
-    if (tid < k) {
-      const uint64_t rid = static_cast<uint64_t>(M.row_offset + row);
-      // restart r draws from the counters t + 16 r
-      uint32_t c[4] = {static_cast<uint32_t>(rid), static_cast<uint32_t>(tid + 16 * restart),
-                       static_cast<uint32_t>(M.matrix_index), static_cast<uint32_t>(rid >> 32)};
-      philox4x32_10(c, static_cast<uint32_t>(args.seed), static_cast<uint32_t>(args.seed >> 32));
-      S.u[tid] = (static_cast<unsigned long long>(c[1]) << 32) | c[0];
-    }
     if (init == INIT_GREEDY && tid < k * (greedy_trials(k) - 1)) {
       // greedy candidates s >= 1 of draw t: counter word t + 16 restart + 65536 s
       const int s = 1 + tid / k, t = tid - (s - 1) * k;
