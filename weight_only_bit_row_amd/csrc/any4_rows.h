@@ -29,8 +29,9 @@
 //              table would need a second switch point in one cell uses a 4-level
 //              binary search over all switch points instead (same result).  The
 //              element then adds (a_j, a_j*w_S_j) in fp64 (the product is exact) into
-//              lane-private LDS bins; bins are reduced per wave in a fixed order
-//              (no global atomics)
+//              lane-private LDS bins, reduced per wave in a fixed order; rows of 5-16
+//              waves add the same terms in 64-bit fixed point (exact integer sums) into
+//              one set of bins for the whole row (no global atomics)
 //   emit       final assignment, nibble packing, fp16 LUT/scale/offset, fp64 objective
 //
 // All float code is compiled with -ffp-contract=off: every squared distance is
@@ -198,6 +199,17 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 __device__ __forceinline__ unsigned long long exact_u64(double v) {
   return static_cast<unsigned long long>(__double_as_longlong(v + 4503599627370496.0)) -
          0x4330000000000000ull;
+}
+// Fixed-point Eq. 23 terms (rows of 5-16 waves): a term t with |t| < 2^51 becomes the
+// nearest integer by one fused add of 1.5 * 2^52, whose result lies in [2^52, 2^53) where
+// doubles are spaced by 1; the bit pattern of that double minus the constant's is the
+// integer in two's complement (one op on the high word).  Integer sums do not depend on
+// their order, so every wave of a row can add into the same bins.
+constexpr double kFixBias = 6755399441055744.0;  // 1.5 * 2^52
+constexpr unsigned long long kFixBiasBits = 0x4338000000000000ull;
+__device__ __forceinline__ unsigned long long fix_term(double u, double v) {
+  return static_cast<unsigned long long>(__double_as_longlong(__builtin_fma(u, v, kFixBias))) -
+         kFixBiasBits;
 }
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
@@ -704,7 +716,7 @@ __device__ __forceinline__ double cvt_f64_in_round(float v, int tok) {
   return r;
 }
 
-template <int E, int KIND, bool TABLE>
+template <int E, int KIND, bool TABLE, bool FIX>
 __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
                                                const uint32_t (&cw)[CellWords<E>::value], const Smem& S,
                                                const unsigned char* table, double* bins, int lane,
@@ -756,8 +768,16 @@ __device__ __forceinline__ double element_pass(float (&x)[E], float (&a)[E],
       const double xd = cvt_f64_in_round(x[m], tok);
       if (KIND != PASS_FINAL) {
         double* b = bins + pos[i] * kBinCols + (lane & (kBinCols - 1));
-        atomicAdd(b, ad);
-        atomicAdd(b + kMaxClusters * kBinCols, ad * xd);
+        if (FIX) {
+          // a is held as a * 2^sigma (< 2^43): S0 takes round(4 a), S1 round(a w_S), both
+          // far below the 2^51 of fix_term (4 is an inline operand of the fused add)
+          unsigned long long* bu = reinterpret_cast<unsigned long long*>(b);
+          atomicAdd(bu, fix_term(ad, 4.0));
+          atomicAdd(bu + kMaxClusters * kBinCols, fix_term(ad, xd));
+        } else {
+          atomicAdd(b, ad);
+          atomicAdd(b + kMaxClusters * kBinCols, ad * xd);
+        }
       }
       if (KIND != PASS_ACCUM) {
         const int q = S.sidx[pos[i]];
@@ -792,6 +812,23 @@ __device__ __forceinline__ double reduce_bins(const double* bins, int lane) {
   }
   const double other = dppd<0xB1>(s);
   return half ? other + s : s + other;  // same order in both lanes of the pair
+}
+
+// The same reduction over fixed-point bins (mod 2^64; the round's sums are exact).
+__device__ __forceinline__ unsigned long long reduce_bins_fix(const double* bins, int lane) {
+  asm volatile("" : "+v"(lane));
+  constexpr int CH = kBinCols / 4;
+  const int slot = lane >> 1, half = lane & 1;
+  const ulonglong2* src = reinterpret_cast<const ulonglong2*>(bins + slot * kBinCols + half * (kBinCols / 2));
+  unsigned long long s = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int j = (i + (lane >> 1) + (CH / 2) * half) & (CH - 1);
+    const ulonglong2 v = src[j];
+    s += v.x;
+    s += v.y;
+  }
+  return s + dpp64<0xB1>(s);
 }
 
 __device__ __forceinline__ void zero_bins(double* bins, int lane) {
@@ -1368,13 +1405,34 @@ void any4_rows_kernel(const LaunchArgs args) {
 #pragma unroll
   for (int m = 0; m < E; ++m)
     cw[m / kCellsPerWord] |= (cell_of(xv[m], G, cell_off) * kCellBytes) << (8 * (m % kCellsPerWord));
+  // Rows of 5-16 waves sum the Eq. 23 terms in 64-bit fixed point, all waves into one
+  // set of bins (wave 0's area), which wave 0 alone reduces after the round's first
+  // barrier: one 8 KB reduction per round instead of one per wave.  Shorter rows keep
+  // per-wave fp64 bins, reduced by every wave before that barrier.
+  constexpr bool FIX = NWMAX > 8;
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
-                 wave * (2 * kMaxClusters * kBinCols);
+                 (FIX ? 0 : wave) * (2 * kMaxClusters * kBinCols);
+  // Fixed-point scale: a * 2^sigma < 2^43 for every sample weight of the row (exact, a
+  // power of two), so S0's terms round(4 a 2^sigma) stay below 2^45 and S1's
+  // round(a 2^sigma w_S) below 2^47 (|w_S| < 16); a round's sums over at most 2^15
+  // columns stay below 2^62 in magnitude, so the bins may wrap mod 2^64 over the rounds
+  // and a round's sums are still exact.  Objectives from the scaled weights are scaled
+  // back by 2^-sigma (exact).
+  int sigma = 0;
+  if (FIX) {
+    int e_amax = 0;
+    if (a_max > 0.0f) frexpf(a_max, &e_amax);
+    sigma = 43 - e_amax;
+#pragma unroll
+    for (int m = 0; m < E; ++m) av[m] = ldexpf(av[m], sigma);
+  }
+  const double j_unscale = FIX ? ldexp(1.0, -sigma) : 1.0;
   uint32_t packed[E / 8];
 #pragma unroll
   for (int v = 0; v < E / 8; ++v) packed[v] = 0;
-  zero_bins(bins, lane);
+  if (!FIX || wave == 0) zero_bins(bins, lane);
   double prev_total = 0.0;  // this lane's slot total after the previous round
+  unsigned long long prev_fix = 0;  // the same for fixed-point bins (wave 0)
   const int rounds = (MODE == MODE_STEP) ? 1 : args.iters;
   // Per round: every wave runs its elements and publishes its reduced bins (one
   // barrier); wave 0 alone updates the centroids and prepares the next round's sorted
@@ -1395,33 +1453,46 @@ void any4_rows_kernel(const LaunchArgs args) {
       uint8_t* arow = M.assign_out + row * K + col0;
       double J = 0.0;
       if (col0 < K) {
-        J = use_table ? element_pass<E, PASS_STEP, true>(xv, av, cw, S, table, bins, lane, arow,
-                                                          packed, n_valid, it)
-                      : element_pass<E, PASS_STEP, false>(xv, av, cw, S, table, bins, lane, arow,
-                                                           packed, n_valid, it);
+        J = use_table ? element_pass<E, PASS_STEP, true, FIX>(xv, av, cw, S, table, bins, lane, arow,
+                                                               packed, n_valid, it)
+                      : element_pass<E, PASS_STEP, false, FIX>(xv, av, cw, S, table, bins, lane, arow,
+                                                                packed, n_valid, it);
       }
-      J = block_sum_f64(J, S, lane, wave, nw);
+      J = block_sum_f64(J * j_unscale, S, lane, wave, nw);
       if (tid == 0 && M.objective) M.objective[row] = J;
     } else if (col0 < K) {
       if (use_table)
-        element_pass<E, PASS_ACCUM, true>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
+        element_pass<E, PASS_ACCUM, true, FIX>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
       else
-        element_pass<E, PASS_ACCUM, false>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
+        element_pass<E, PASS_ACCUM, false, FIX>(xv, av, cw, S, table, bins, lane, nullptr, packed, n_valid, it);
     }
     // the bin reduction and wave 0's centroid update are the round's serial chain: raised
     // priority, as in seeding, until the round's second barrier
     __builtin_amdgcn_s_setprio(2);
-    // the reduction reads bins that other lanes of this wave just added to
-    wave_lds_fence();
-    const double total = reduce_bins(bins, lane);
-    if ((lane & 1) == 0) S.wred[wave][lane >> 1] = total - prev_total;
-    prev_total = total;
+    if (!FIX) {
+      // the reduction reads bins that other lanes of this wave just added to
+      wave_lds_fence();
+      const double total = reduce_bins(bins, lane);
+      if ((lane & 1) == 0) S.wred[wave][lane >> 1] = total - prev_total;
+      prev_total = total;
+    }
     __syncthreads();
     if (wave == 0) {
+      if (FIX) {
+        // every wave's terms are in: the round's exact sums, in units of 2^-sigma (S0
+        // scaled back from its factor 4, exactly), so that S1 / S0 is the weighted mean
+        const unsigned long long total = reduce_bins_fix(bins, lane);
+        if ((lane & 1) == 0) {
+          const double d = static_cast<double>(static_cast<long long>(total - prev_fix));
+          S.wred[0][lane >> 1] = (lane >> 1) < kMaxClusters ? d * 0.25 : d;
+        }
+        prev_fix = total;
+        wave_lds_fence();
+      }
       float t;
       uint32_t tc;
       bool same;
-      U = update_and_structure(S, nw, k, G, cell_off, lane, U, sv, si, t, tc, same);
+      U = update_and_structure(S, FIX ? 1 : nw, k, G, cell_off, lane, U, sv, si, t, tc, same);
       build_table(S, table, lane, t, tc, U);
       if (lane == 0) S.done = same ? 1 : 0;
     }
@@ -1439,10 +1510,10 @@ void any4_rows_kernel(const LaunchArgs args) {
   const bool use_table = S.use_table != 0;
   double J = 0.0;
   if (col0 < K) {
-    J = use_table ? element_pass<E, PASS_FINAL, true>(xv, av, cw, S, table, bins, lane, nullptr,
-                                                       packed, n_valid, rounds)
-                  : element_pass<E, PASS_FINAL, false>(xv, av, cw, S, table, bins, lane, nullptr,
-                                                        packed, n_valid, rounds);
+    J = use_table ? element_pass<E, PASS_FINAL, true, FIX>(xv, av, cw, S, table, bins, lane, nullptr,
+                                                            packed, n_valid, rounds)
+                  : element_pass<E, PASS_FINAL, false, FIX>(xv, av, cw, S, table, bins, lane, nullptr,
+                                                             packed, n_valid, rounds);
   }
   if (col0 < K) {
     uint8_t* dst = M.codes + row * (K / 2) + col0 / 2;
@@ -1459,7 +1530,7 @@ void any4_rows_kernel(const LaunchArgs args) {
         if (m < n_valid) dst[m / 2] = static_cast<uint8_t>(packed[m / 8] >> (4 * (m % 8)));
     }
   }
-  J = block_sum_f64(J, S, lane, wave, nw);
+  J = block_sum_f64(J * j_unscale, S, lane, wave, nw);
   if (tid == 0 && M.objective) M.objective[row] = J;
   if (tid < k) {
     M.lut[row * k + tid] = f16_bits(S.c[tid]);
