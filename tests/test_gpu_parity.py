@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import (OBJECTIVE_REL, centroid_close, check_rows, excused_mismatch, say, to_device,
-                         unpack_codes, widen)
+from parity_util import (OBJECTIVE_REL, centroid_close, check_rows, excused_mismatch, oracle_row_inputs,
+                         say, to_device, unpack_codes, widen)
 from workloads import BF16, F32, make, make_matrix
 
 pytestmark = pytest.mark.gpu
@@ -404,3 +404,51 @@ def test_layer_batch_sampled_rows(bits):
         same, dj = _check_sampled(m, o, cf, pk, wl.group, wl.n_clusters, wl.iters, rows)
         say(f"  any{bits} {m.name} {m.w.shape}: {same.sum()}/{rows.size} sampled rows identical, "
             f"dJ/J {dj:.2e}")
+
+
+# Rows of 5-16 waves sum the Eq. 23 terms in 64-bit fixed point scaled to the row's
+# largest sample weight.  Weights spread over 2^40 (a tenth of the channels scaled by
+# 2^-28, one in a hundred by 2^12) must still give the oracle's rounds and codes, also
+# under symmetric scaling, where w_S and so the S1 terms are negative.
+WIDE_SPAN = [("five_waves_k10240", 4, 10240, BF16, 128, 16, 51, 0),
+             ("fourteen_waves_k28672", 2, 28672, BF16, 128, 16, 52, 0),
+             ("seven_waves_symmetric_k14336", 3, 14336, BF16, 128, 16, 53, 1 << 4)]
+
+
+@pytest.mark.parametrize("shape", WIDE_SPAN, ids=[s[0] for s in WIDE_SPAN])
+def test_fixed_point_sums_wide_weight_span(shape):
+    name, N, K, dtype, g, k, seed, variant = shape
+    say(f"fixed-point M-step, wide weight span {name}")
+    m = make_matrix(name, N, K, dtype, seed)
+    rng = np.random.default_rng(seed)
+    act = m.act.astype(np.float64)
+    small = rng.choice(K, K // 10, replace=False)
+    act[small] *= 2.0 ** -28
+    act[rng.choice(np.setdiff1d(np.arange(K), small), K // 100, replace=False)] *= 2.0 ** 12
+    m.act = act.astype(np.float32)
+    w, act_d = to_device(m)
+    # one round from the oracle's centroids: assignments up to near-ties, M-step within
+    # tolerance of the oracle's on the GPU's assignment
+    iters = 8
+    ref = oracle.quantize(m.w, m.dtype, m.act, g, k, iters, trace=True, variant=variant)
+    for t in (0, 3):
+        c_in = torch.from_numpy(ref["c_trace"][:, t, :].copy()).cuda()
+        assign, c_out, _ = any4().stage_lloyd_step(w, act_d, c_in, group=g, n_clusters=k, variant=variant)
+        torch.cuda.synchronize()
+        assign, c_out = assign.cpu().numpy(), c_out.cpu().numpy()
+        for i in range(N):
+            ws, a = oracle_row_inputs(m.w[i], m.dtype, m.act, g, k, variant)
+            c_t = ref["c_trace"][i, t]
+            diff, ok = excused_mismatch(ws, c_t, oracle.estep_row(ws, c_t), assign[i])
+            assert ok.all(), (name, i, t, diff[~ok][:5])
+            c_ref = oracle.mstep_row(ws, a, assign[i].astype(np.int32), c_t)
+            assert centroid_close(c_out[i], c_ref).all(), (name, i, t, c_out[i], c_ref)
+    # the whole path: picks exact, every row identical or explained
+    out, c_final, picks, ws_buf = any4().stage_full(w, act_d, group=g, n_clusters=k, iters=iters,
+                                                    seed=0, variant=variant)
+    torch.cuda.synchronize()
+    assert any4().read_status(ws_buf) == 0
+    assert np.array_equal(picks.cpu().numpy(), ref["picks"])
+    same = check_rows(any4(), m, g, k, iters, 0, out.codes.cpu().numpy(), c_final.cpu().numpy(),
+                      out.lut.cpu().numpy().view(np.uint16), ref, np.arange(N), variant=variant)
+    say(f"  {name}: rows with identical codes {same.mean():.4f}")
