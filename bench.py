@@ -18,7 +18,8 @@ Beside `value` (after the timed quantizer steps, not part of it) the same line r
                 Lloyd elem-iters/s from t(20 rounds) - t(0) and the credited FP32 share;
   bookends      E|x| of a calibration batch, the Eq. 4 dequantization and the LUT
                 matrix-vector products against the HBM roofline;
-  sorted_lloyd  the sorted-row Lloyd stage on the headline matrix;
+  sorted_lloyd  the sorted-row Lloyd stage on the headline matrix (and, as
+                sorted_lloyd_long_rows, on the Llama3-70B down_proj, sorted in halves);
   cpu_baseline  the oracle on the host, on one pinned core and on all usable cores (at
                 most 16), for every workload, measured before the GPU is touched.
 
@@ -177,7 +178,8 @@ def sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, stream, n_launches
     launch stream.  `rows_identical` compares its centroids with the register path's."""
     ws_, _, _, a = any4.stage_scale(w, act, group=g, n_clusters=k)
     c0, _ = any4.stage_seed(w, act, group=g, n_clusters=k)
-    res = {"kernel": "sorted_lloyd_kernel", "n_rows": int(w.shape[0]), "n_cols": int(w.shape[1])}
+    kern = "sorted_lloyd_kernel" if w.shape[1] <= 16384 else "sorted_lloyd_split_kernel"
+    res = {"kernel": kern, "n_rows": int(w.shape[0]), "n_cols": int(w.shape[1])}
     for n_it in (0, iters):
         c = any4.stage_lloyd_sorted(ws_, a, c0, n_clusters=k, iters=n_it, group=g)
         torch.cuda.synchronize()
@@ -585,6 +587,15 @@ def main():
         line["bookends"] = bookends(any4, torch, np, out, N, K, g, k, dev, stream)
         _, c_reg, _, _ = any4.stage_full(w, act, g, k, iters, seed=0)
         line["sorted_lloyd"] = sorted_lloyd(any4, torch, np, w, act, g, k, iters, c_reg, stream)
+        if "down_70b" in wls:
+            # rows past 16384 columns: the stage sorts each row as two halves
+            m70 = wls["down_70b"].matrices[0]
+            w70 = torch.from_numpy(m70.w.view(np.int16)).to(dev).view(torch.bfloat16)
+            a70 = torch.from_numpy(m70.act).to(dev)
+            _, c70, _, _ = any4.stage_full(w70, a70, g, k, iters, seed=0)
+            line["sorted_lloyd_long_rows"] = sorted_lloyd(any4, torch, np, w70, a70, g, k, iters, c70, stream,
+                                                          n_launches=2)
+            del w70, a70, c70
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line))

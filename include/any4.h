@@ -179,13 +179,25 @@ int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const
  * rule is the same as any4_quantize's, so the fixed points are too; the sums differ
  * only in fp64 rounding order.  Uses m->n_rows and m->n_cols only (other fields
  * ignored); params->group is checked but unused and the symmetric flag of
- * params->variant selects the scaled range.  Rows of at most 16384 columns, the sorted
- * row held in LDS (ANY4_ERR_UNSUPPORTED beyond); ANY4_ERR_INVALID_ARG for a NULL pointer with
- * n_rows > 0, n_cols < 2 or odd, or bad params.  A row holding a non-finite w_s or a
- * (which any4_stage_scale reports through its status) gives unspecified centroids for
- * that row only.  The caller owns every buffer.  Asynchronous on `stream`. */
+ * params->variant selects the scaled range.  Rows of at most 16384 columns are sorted
+ * in LDS and need no workspace (workspace may be NULL); rows of 16386 to 32768 columns
+ * are sorted as two halves and keep their sorted sample weights in `workspace` (device,
+ * 16-byte aligned, at least any4_stage_lloyd_sorted_workspace_bytes(N, K) bytes, else
+ * ANY4_ERR_WORKSPACE; its contents on entry do not matter and it may be reused once
+ * the call has completed on `stream`).  ANY4_ERR_UNSUPPORTED past 32768 columns;
+ * ANY4_ERR_INVALID_ARG for a NULL pointer with n_rows > 0, n_cols < 2 or odd, or bad
+ * params.  A row holding a non-finite w_s or a (which any4_stage_scale reports through
+ * its status) gives unspecified centroids for that row only.  The caller owns every
+ * buffer.  Asynchronous on `stream`. */
 int any4_stage_lloyd_sorted(const any4_matrix* m, const any4_params* params, const float* w_s,
-                            const float* a, const float* c_in, float* c_out, hipStream_t stream);
+                            const float* a, const float* c_in, float* c_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes any4_stage_lloyd_sorted needs for n_rows rows of n_cols columns, in
+ * *bytes_out: 0 up to 16384 columns, n_rows * 3 * 16384 * 4 from 16386 to 32768.
+ * Host-only.  ANY4_ERR_INVALID_ARG for a NULL bytes_out, n_rows < 0, or n_cols < 2 or
+ * odd; ANY4_ERR_UNSUPPORTED past 32768 columns or 2^31 rows. */
+int any4_stage_lloyd_sorted_workspace_bytes(int64_t n_rows, int64_t n_cols, size_t* bytes_out);
 
 /* Emission only: codes, lut, scale, offset of `m` from assign [N,K] uint8,
  * c [N, n_clusters] fp32, alpha/beta [N, K/group] fp32 (Section 2.4.1 layout). */

@@ -120,11 +120,20 @@ int main() {
   EXPECT(any4_stage_seed(&m, &p, f, static_cast<int32_t*>(P(0xB000)), nullptr), ANY4_OK);
   EXPECT(any4_stage_seed(&m, &p, nullptr, nullptr, nullptr), ANY4_ERR_INVALID_ARG);
   EXPECT(any4_stage_lloyd_step(&m, &p, f, static_cast<uint8_t*>(P(0xC000)), f, nullptr, nullptr), ANY4_OK);
-  EXPECT(any4_stage_lloyd_sorted(&m, &p, f, f, f, f, nullptr), ANY4_OK);
-  any4_matrix m17k = mat(2, 16386);   // past the sorted stage's 16384 columns
+  EXPECT(any4_stage_lloyd_sorted(&m, &p, f, f, f, f, nullptr, 0, nullptr), ANY4_OK);
+  any4_matrix m17k = mat(2, 16386);   // past 16384 columns: two halves and a workspace
   any4_params g8 = p;
   g8.group = 8;
-  EXPECT(any4_stage_lloyd_sorted(&m17k, &g8, f, f, f, f, nullptr), ANY4_ERR_UNSUPPORTED);
+  EXPECT(any4_stage_lloyd_sorted_workspace_bytes(2, 16386, &bytes), ANY4_OK);
+  EXPECT(bytes == 2u * 3u * 16384u * 4u ? 1 : 0, 1);
+  EXPECT(any4_stage_lloyd_sorted(&m17k, &g8, f, f, f, f, nullptr, 0, nullptr), ANY4_ERR_WORKSPACE);
+  EXPECT(any4_stage_lloyd_sorted(&m17k, &g8, f, f, f, f, P(0xD000), bytes - 1, nullptr), ANY4_ERR_WORKSPACE);
+  EXPECT(any4_stage_lloyd_sorted(&m17k, &g8, f, f, f, f, P(0xD000), bytes, nullptr), ANY4_OK);
+  any4_matrix m33k = mat(2, 32770);   // past 32768 columns
+  EXPECT(any4_stage_lloyd_sorted(&m33k, &g8, f, f, f, f, P(0xD000), bytes, nullptr), ANY4_ERR_UNSUPPORTED);
+  EXPECT(any4_stage_lloyd_sorted_workspace_bytes(2, 32770, &bytes), ANY4_ERR_UNSUPPORTED);
+  EXPECT(any4_stage_lloyd_sorted_workspace_bytes(2, 4096, &bytes), ANY4_OK);
+  EXPECT(bytes == 0 ? 1 : 0, 1);
   EXPECT(any4_stage_pack(&m, &p, static_cast<uint8_t*>(P(0xC000)), f, f, f, nullptr), ANY4_OK);
   EXPECT(any4_stage_full(&m, &p, f, nullptr, ws256, sizeof(ws256), nullptr), ANY4_OK);
   EXPECT(any4_stage_full(&m, &p, f, nullptr, nullptr, 0, nullptr), ANY4_ERR_WORKSPACE);

@@ -51,7 +51,11 @@ hipError_t launch_pack(const MatDesc&, int, int, const uint8_t*, const float*, c
   return hipSuccess;
 }
 hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t) {
-  return (d.n_cols >= 2 && d.n_cols <= kSortedMaxCols) ? hipSuccess : hipErrorInvalidValue;
+  if (d.n_cols < 2 || d.n_cols > 2 * kSortedMaxCols) return hipErrorInvalidValue;
+  return (d.n_cols <= kSortedMaxCols || d.work) ? hipSuccess : hipErrorInvalidValue;
+}
+size_t sorted_lloyd_work_bytes(int64_t n_rows, int64_t n_cols) {
+  return n_cols > kSortedMaxCols ? static_cast<size_t>(n_rows) * 3 * sizeof(float) * kSortedMaxCols : 0;
 }
 hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t) {
   return (d.cand_codes && d.codes && d.best_obj) ? hipSuccess : hipErrorInvalidValue;

@@ -205,21 +205,37 @@ def test_lut_gemv_validates_before_launch(L):
 
 def test_sorted_lloyd_validates_before_launch(L):
     """any4_stage_lloyd_sorted rejects bad params, missing buffers and odd or short rows
-    (invalid argument) and rows over 16384 columns (unsupported) without a HIP call; an
-    empty matrix is a no-op."""
+    (invalid argument), rows over 16384 columns without their workspace (workspace) and
+    rows over 32768 columns (unsupported), all without a HIP call; an empty matrix is a
+    no-op."""
     p = any4.params(128, 16, 20, 0)
     f = L.any4_stage_lloyd_sorted
     buf = 0x8000
-    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), None, buf, buf, buf, None) == 1
-    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), buf, buf, buf, None, None) == 1
-    assert f(ctypes.byref(_mat(k=511)), ctypes.byref(p), buf, buf, buf, buf, None) == 1
-    assert f(ctypes.byref(_mat(k=0)), ctypes.byref(p), buf, buf, buf, buf, None) == 1
-    assert f(None, ctypes.byref(p), buf, buf, buf, buf, None) == 1
-    assert f(ctypes.byref(_mat(k=512)), ctypes.byref(any4.params(128, 5)), buf, buf, buf, buf, None) == 1
-    assert f(ctypes.byref(_mat(k=16386)), ctypes.byref(p), buf, buf, buf, buf, None) == 2
+    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), None, buf, buf, buf, None, 0, None) == 1
+    assert f(ctypes.byref(_mat(k=4096)), ctypes.byref(p), buf, buf, buf, None, None, 0, None) == 1
+    assert f(ctypes.byref(_mat(k=511)), ctypes.byref(p), buf, buf, buf, buf, None, 0, None) == 1
+    assert f(ctypes.byref(_mat(k=0)), ctypes.byref(p), buf, buf, buf, buf, None, 0, None) == 1
+    assert f(None, ctypes.byref(p), buf, buf, buf, buf, None, 0, None) == 1
+    assert f(ctypes.byref(_mat(k=512)), ctypes.byref(any4.params(128, 5)), buf, buf, buf, buf, None, 0,
+             None) == 1
+    need = ctypes.c_size_t(0)
+    assert L.any4_stage_lloyd_sorted_workspace_bytes(4, 16386, ctypes.byref(need)) == 0
+    assert need.value == 4 * 3 * 16384 * 4
+    g2 = any4.params(2, 16, 20, 0)
+    assert f(ctypes.byref(_mat(k=16386)), ctypes.byref(g2), buf, buf, buf, buf, None, 0, None) == 3
+    assert f(ctypes.byref(_mat(k=16386)), ctypes.byref(g2), buf, buf, buf, buf, 0x9000,
+             need.value - 1, None) == 3
+    assert f(ctypes.byref(_mat(k=16386)), ctypes.byref(g2), buf, buf, buf, buf, 0x9008,
+             need.value, None) == 3   # misaligned
+    assert f(ctypes.byref(_mat(k=32770)), ctypes.byref(g2), buf, buf, buf, buf, 0x9000,
+             need.value, None) == 2
+    assert L.any4_stage_lloyd_sorted_workspace_bytes(4, 32770, ctypes.byref(need)) == 2
+    assert L.any4_stage_lloyd_sorted_workspace_bytes(4, 4096, ctypes.byref(need)) == 0
+    assert need.value == 0
+    assert L.any4_stage_lloyd_sorted_workspace_bytes(4, 4095, ctypes.byref(need)) == 1
     m0 = any4.Any4Matrix()
     m0.n_rows, m0.n_cols = 0, 256
-    assert f(ctypes.byref(m0), ctypes.byref(p), None, None, None, None, None) == 0
+    assert f(ctypes.byref(m0), ctypes.byref(p), None, None, None, None, None, 0, None) == 0
 
 
 def test_launch_geometry(L):

@@ -35,6 +35,11 @@ SHAPES = [
     ("down_proj_k14336", 4, 14336, BF16, 128, 16, 20, 0, 308),
     ("max_k16384_any3_sym", 3, 16384, BF16, 64, 8, 20, SYM, 309),
     ("ragged_k10002_g2", 3, 10002, F32, 2, 16, 12, W_NONE, 310),
+    # rows past 16384 columns, sorted as two halves with the sorted weights in the
+    # workspace: the 70B down_proj length, the longest supported row, the shortest one
+    ("down_70b_k28672", 2, 28672, BF16, 128, 16, 20, 0, 312),
+    ("max_k32768_any3_sym", 2, 32768, BF16, 64, 8, 20, SYM, 313),
+    ("ragged_k16386_g2", 2, 16386, F32, 2, 16, 12, W_NONE, 314),
 ]
 
 
@@ -180,9 +185,26 @@ def test_sorted_lloyd_is_deterministic_and_agrees_with_the_register_path():
     say(f"  rows identical to the register path: {n_same}/32")
 
 
+def test_sorted_lloyd_split_rows_ignore_the_workspace_contents():
+    """Rows over 16384 columns keep their sorted weights in the workspace: a caller's
+    workspace full of NaN bytes, and a second call reusing it, give the same bits as a
+    fresh one."""
+    m = make_matrix("split_ws", 3, 20480, BF16, 315)
+    ws, a, c0 = oracle_inputs(m, 128, 16, 0, 0)
+    dev = torch.device("cuda")
+    args = (torch.from_numpy(ws).to(dev), torch.from_numpy(a).to(dev), torch.from_numpy(c0).to(dev))
+    ref = any4().stage_lloyd_sorted(*args, n_clusters=16, iters=20).cpu().numpy()
+    work = torch.full((3 * 3 * 16384,), float("nan"), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        c = any4().stage_lloyd_sorted(*args, n_clusters=16, iters=20, ws=work).cpu().numpy()
+        assert np.array_equal(c.view(np.uint32), ref.view(np.uint32))
+    with pytest.raises(ValueError):
+        any4().stage_lloyd_sorted(*args, n_clusters=16, iters=20, ws=work[:-1])
+
+
 def test_sorted_lloyd_rejects_long_rows_and_bad_shapes():
     dev = torch.device("cuda")
-    ws = torch.zeros((2, 16386), device=dev)
+    ws = torch.zeros((2, 32770), device=dev)
     c0 = torch.zeros((2, 16), device=dev)
     with pytest.raises(any4().Any4Error):
         any4().stage_lloyd_sorted(ws, ws, c0)

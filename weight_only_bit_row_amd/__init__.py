@@ -34,7 +34,8 @@ EXPORTED = [
     "any4_workspace_bytes", "any4_quantize", "any4_read_device_status", "any4_status_string",
     "any4_launch_geometry",
     "any4_stage_scale", "any4_stage_seed", "any4_stage_lloyd_step", "any4_stage_pack",
-    "any4_stage_full", "any4_stage_lloyd_sorted", "any4_stage_quantize_batch",
+    "any4_stage_full", "any4_stage_lloyd_sorted", "any4_stage_lloyd_sorted_workspace_bytes",
+    "any4_stage_quantize_batch",
     "any4_quantize_noalloc",
     "any4_act_absmean_workspace_bytes", "any4_act_absmean", "any4_dequantize", "any4_lut_gemv",
 ]
@@ -93,7 +94,9 @@ def lib():
         L.any4_stage_scale.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_seed.argtypes = [MP, PP, P, P, P]
         L.any4_stage_lloyd_step.argtypes = [MP, PP, P, P, P, P, P]
-        L.any4_stage_lloyd_sorted.argtypes = [MP, PP, P, P, P, P, P]
+        L.any4_stage_lloyd_sorted.argtypes = [MP, PP, P, P, P, P, P, ctypes.c_size_t, P]
+        L.any4_stage_lloyd_sorted_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
+                                                               ctypes.POINTER(ctypes.c_size_t)]
         L.any4_stage_pack.argtypes = [MP, PP, P, P, P, P, P]
         L.any4_stage_full.argtypes = [MP, PP, P, P, P, ctypes.c_size_t, P]
         L.any4_stage_quantize_batch.argtypes = [MP, ctypes.c_int32, PP, P, P, P, ctypes.c_size_t, P]
@@ -464,9 +467,10 @@ def stage_lloyd_step(w, act, c_in, group=128, n_clusters=16, variant=0):
     return assign, c_out, obj
 
 
-def stage_lloyd_sorted(w_s, a, c_in, n_clusters=16, iters=20, variant=0, group=128):
+def stage_lloyd_sorted(w_s, a, c_in, n_clusters=16, iters=20, variant=0, group=128, ws=None):
     """Sorted-row Lloyd: ``iters`` rounds from c_in [N, n_clusters] on the scaled rows
-    w_s and sample weights a ([N, K] fp32, K <= 16384); returns c_out [N, n_clusters]."""
+    w_s and sample weights a ([N, K] fp32, K <= 32768); returns c_out [N, n_clusters].
+    Rows over 16384 columns need a workspace (made here unless ``ws`` is given)."""
     torch = _torch()
     _require_gpu(w_s)
     N, K = w_s.shape
@@ -477,12 +481,21 @@ def stage_lloyd_sorted(w_s, a, c_in, n_clusters=16, iters=20, variant=0, group=1
         raise ValueError("a must be [N, K] and c_in [N, n_clusters]")
     if a.device != w_s.device or c_in.device != w_s.device:
         raise ValueError("w_s, a and c_in must be on one device")
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().any4_stage_lloyd_sorted_workspace_bytes(N, K, ctypes.byref(nbytes)),
+           "any4_stage_lloyd_sorted_workspace_bytes")
+    if nbytes.value and ws is None:
+        ws = torch.empty((nbytes.value,), dtype=torch.uint8, device=w_s.device)
+    if ws is not None and (ws.device != w_s.device or ws.numel() * ws.element_size() < nbytes.value):
+        raise ValueError("ws must be on w_s's device and hold the sorted stage's workspace")
     c_out = torch.empty((N, n_clusters), dtype=torch.float32, device=w_s.device)
     m = Any4Matrix()
     m.n_rows, m.n_cols = N, K
     p = params(group, n_clusters, iters, 0, variant)
     _check(lib().any4_stage_lloyd_sorted(ctypes.byref(m), ctypes.byref(p), _ptr(w_s), _ptr(a),
-                                         _ptr(c_in), _ptr(c_out), _stream(w_s.device)),
+                                         _ptr(c_in), _ptr(c_out), _ptr(ws) if ws is not None else None,
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         _stream(w_s.device)),
            "any4_stage_lloyd_sorted")
     return c_out
 

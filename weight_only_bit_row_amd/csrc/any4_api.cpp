@@ -397,19 +397,32 @@ int any4_stage_lloyd_step(const any4_matrix* m, const any4_params* params, const
   return launch_one(make_args(params, 1, nullptr), d, any4::MODE_STEP, stream);
 }
 
+int any4_stage_lloyd_sorted_workspace_bytes(int64_t n_rows, int64_t n_cols, size_t* bytes_out) {
+  if (!bytes_out || n_rows < 0 || n_cols < 2 || (n_cols & 1)) return ANY4_ERR_INVALID_ARG;
+  if (n_cols > 2 * static_cast<int64_t>(any4::kSortedMaxCols) || n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  *bytes_out = any4::sorted_lloyd_work_bytes(n_rows, n_cols);
+  return ANY4_OK;
+}
+
 int any4_stage_lloyd_sorted(const any4_matrix* m, const any4_params* params, const float* w_s,
-                            const float* a, const float* c_in, float* c_out, hipStream_t stream) {
+                            const float* a, const float* c_in, float* c_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   const int st = check_params(params);
   if (st != ANY4_OK) return st;
   if (!m || m->n_rows < 0 || m->n_cols < 2 || (m->n_cols & 1)) return ANY4_ERR_INVALID_ARG;
-  if (m->n_cols > any4::kSortedMaxCols || m->n_rows > INT32_MAX) return ANY4_ERR_UNSUPPORTED;
+  if (m->n_cols > 2 * static_cast<int64_t>(any4::kSortedMaxCols) || m->n_rows > INT32_MAX)
+    return ANY4_ERR_UNSUPPORTED;
   if (m->n_rows == 0) return ANY4_OK;
   if (!w_s || !a || !c_in || !c_out) return ANY4_ERR_INVALID_ARG;
+  const size_t need = any4::sorted_lloyd_work_bytes(m->n_rows, m->n_cols);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15)))
+    return ANY4_ERR_WORKSPACE;
   any4::SortedDesc d{};
   d.w_s = w_s;
   d.a = a;
   d.c_in = c_in;
   d.c_out = c_out;
+  d.work = need > 0 ? static_cast<float*>(workspace) : nullptr;
   d.n_rows = m->n_rows;
   d.n_cols = static_cast<int32_t>(m->n_cols);
   d.n_clusters = params->n_clusters;

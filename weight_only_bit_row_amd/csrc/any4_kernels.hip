@@ -122,32 +122,16 @@ __device__ __forceinline__ void sort_small_strides(float* key, float* wt, int ti
   }
 }
 
-// PER: compare pairs per thread in an LDS step, kp / 512 for the largest kp of the instance
+// Bitonic sort of kp (a power of two) (key, wt) pairs in LDS, ascending by key; each
+// step pairs lo and lo + stride inside blocks of 2 * stride, the direction set by the
+// bit `size` of lo.  A thread's pairs of a step (pair i = tid + 256 r) are all loaded
+// before any is compared and stored, so their LDS reads are in flight together; every
+// index belongs to one pair per step.  With kSortedRegs elements per thread
+// (kp = 4096), the steps of stride below kSortedRegs stay inside a thread's consecutive
+// elements and run in registers.  PER: compare pairs per thread, kp / 512 for the
+// largest kp of the instance.  Ends with a block barrier.
 template <int PER>
-__global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
-  const int K = d.n_cols, kp = d.kp, k = d.n_clusters, tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  float* key = reinterpret_cast<float*>(smem_raw + kSmemHdr);
-  float* wt = key + kp;
-  double* tot = reinterpret_cast<double*>(wt + kp);  // [2][kSortedThreads + 1]
-  constexpr int TB = kSortedThreads + 1;
-  const int64_t row = blockIdx.x;
-  const float* ws = d.w_s + row * K;
-  const float* ar = d.a + row * K;
-  for (int i = tid; i < kp; i += kSortedThreads) {
-    key[i] = i < K ? ws[i] : __builtin_huge_valf();
-    wt[i] = i < K ? ar[i] : 0.0f;
-  }
-  if (tid < k) S.c[tid] = d.c_in[row * k + tid];
-  __syncthreads();
-  // bitonic sort, ascending by key; each step pairs lo and lo + stride inside blocks of
-  // 2 * stride, the direction set by the bit `size` of lo.  A thread's pairs of a step
-  // (pair i = tid + 256 r) are all loaded before any is compared and stored, so their
-  // LDS reads are in flight together; every index belongs to one pair per step.
-  // With kSortedRegs elements per thread (kp = 4096), the steps of stride below
-  // kSortedRegs stay inside a thread's consecutive elements and run in registers.
+__device__ __forceinline__ void sort_pairs(float* key, float* wt, int kp, int tid) {
   const int half = kp / 2;
   const bool regs = kp == kSortedThreads * kSortedRegs;
   for (int size = 2; size <= kp; size <<= 1) {
@@ -197,10 +181,16 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
       __syncthreads();
     }
   }
-  // fp64 prefix sums in sorted order: thread t sums chunk t (C consecutive elements, in
-  // order), thread 0 turns the chunk totals into chunk bases in thread order, and
-  // P(i) = base of chunk i / C plus the chunk's elements before i, added in order (one
-  // fixed order, so the sums are deterministic)
+}
+
+// fp64 prefix sums of the first K sorted pairs at the starts of 256 chunks of
+// C = ceil(K / 256) elements: thread t sums chunk t in order, thread 0 turns the chunk
+// totals into chunk bases in thread order (tot[t] = P0 before chunk t, tot[TB + t] = P1,
+// tot[256] and tot[TB + 256] the row's totals).  P(i) is then the base of chunk i / C
+// plus the chunk's elements before i, added in order: one fixed order, so every sum is
+// deterministic.  Ends with a block barrier.
+constexpr int kSortedTB = kSortedThreads + 1;
+__device__ __forceinline__ void chunk_bases(const float* key, const float* wt, int K, double* tot, int tid) {
   const int C = (K + kSortedThreads - 1) / kSortedThreads;
   {
     const int b0 = min(K, tid * C), b1 = min(K, b0 + C);
@@ -211,22 +201,76 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
       s1 += av * static_cast<double>(key[i]);
     }
     tot[tid] = s0;
-    tot[TB + tid] = s1;
+    tot[kSortedTB + tid] = s1;
   }
   __syncthreads();
   if (tid == 0) {
     double r0 = 0.0, r1 = 0.0;
     for (int t = 0; t < kSortedThreads; ++t) {
-      const double v0 = tot[t], v1 = tot[TB + t];
+      const double v0 = tot[t], v1 = tot[kSortedTB + t];
       tot[t] = r0;
-      tot[TB + t] = r1;
+      tot[kSortedTB + t] = r1;
       r0 += v0;
       r1 += v1;
     }
     tot[kSortedThreads] = r0;
-    tot[TB + kSortedThreads] = r1;
+    tot[kSortedTB + kSortedThreads] = r1;
   }
   __syncthreads();
+}
+
+// Number of the first n keys below th (keys ascending).
+__device__ __forceinline__ int keys_below(const float* key, int n, float th) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (key[mid] < th)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Per lane p < U of wave 0: the Eq. 23 sums of sorted position p from the prefix sums
+// (q0, q1) at its right end; writes them to S.wred[0] for update_and_structure.
+__device__ __forceinline__ void publish_position_sums(Smem& S, int lane, int U, double q0, double q1) {
+  const double p0 = __shfl_up(q0, 1), p1 = __shfl_up(q1, 1);
+  if (lane < kMaxClusters) {
+    double c0 = 0.0, c1 = 0.0;
+    if (lane < U) {
+      c0 = (lane == 0) ? q0 : q0 - p0;
+      c1 = (lane == 0) ? q1 : q1 - p1;
+      if (!(c0 > 0.0)) c0 = c1 = 0.0;  // an empty range (or an unordered pair) adds nothing
+    }
+    S.wred[0][lane] = c0;
+    S.wred[0][kMaxClusters + lane] = c1;
+  }
+  wave_lds_fence();
+}
+
+template <int PER>
+__global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const SortedDesc d) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
+  const int K = d.n_cols, kp = d.kp, k = d.n_clusters, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  float* key = reinterpret_cast<float*>(smem_raw + kSmemHdr);
+  float* wt = key + kp;
+  double* tot = reinterpret_cast<double*>(wt + kp);  // [2][kSortedThreads + 1]
+  constexpr int TB = kSortedTB;
+  const int64_t row = blockIdx.x;
+  const float* ws = d.w_s + row * K;
+  const float* ar = d.a + row * K;
+  for (int i = tid; i < kp; i += kSortedThreads) {
+    key[i] = i < K ? ws[i] : __builtin_huge_valf();
+    wt[i] = i < K ? ar[i] : 0.0f;
+  }
+  if (tid < k) S.c[tid] = d.c_in[row * k + tid];
+  __syncthreads();
+  sort_pairs<PER>(key, wt, kp, tid);
+  chunk_bases(key, wt, K, tot, tid);
+  const int C = (K + kSortedThreads - 1) / kSortedThreads;
   // the rounds run on wave 0 alone (no block barrier from here on)
   if (tid >= kWave) return;
   const float off = d.symmetric ? static_cast<float>(k / 2) : 0.0f;
@@ -238,44 +282,126 @@ __global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_kernel(const Sort
   for (int it = 0; it < d.iters; ++it) {
     // lane p < U - 1: the number of keys below switch point p (elements at or above it
     // sit right of sorted position p, the register path's rule)
-    int idx = K;
-    if (lane + 1 < U) {
-      const float th = S.thr[lane];
-      int lo = 0, hi = K;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (key[mid] < th)
-          lo = mid + 1;
-        else
-          hi = mid;
-      }
-      idx = lo;
-    }
+    const int idx = (lane + 1 < U) ? keys_below(key, K, S.thr[lane]) : K;
     // prefix sums at the switch index (lane p < U - 1) or at K (the last position)
     double q0 = 0.0, q1 = 0.0;
     if (lane < U) {
-      const int at = (lane + 1 < U) ? idx : K;
-      const int ch = min(at / C, kSortedThreads);
+      const int ch = min(idx / C, kSortedThreads);
       q0 = tot[ch];
       q1 = tot[TB + ch];
-      for (int i = ch * C; i < at; ++i) {
+      for (int i = ch * C; i < idx; ++i) {
         const double av = wt[i];
         q0 += av;
         q1 += av * static_cast<double>(key[i]);
       }
     }
-    const double p0 = __shfl_up(q0, 1), p1 = __shfl_up(q1, 1);
-    if (lane < kMaxClusters) {
-      double c0 = 0.0, c1 = 0.0;
-      if (lane < U) {
-        c0 = (lane == 0) ? q0 : q0 - p0;
-        c1 = (lane == 0) ? q1 : q1 - p1;
-        if (!(c0 > 0.0)) c0 = c1 = 0.0;  // an empty range (or an unordered pair) adds nothing
-      }
-      S.wred[0][lane] = c0;
-      S.wred[0][kMaxClusters + lane] = c1;
+    publish_position_sums(S, lane, U, q0, q1);
+    bool same;
+    U = update_and_structure(S, 1, k, G, off, lane, U, sv, si, t, tc, same);
+  }
+  if (lane < k) d.c_out[row * k + lane] = S.c[lane];
+}
+
+// Rows of kSortedMaxCols + 2 .. 2 kSortedMaxCols columns: the row is sorted as two
+// halves, A = columns [0, K/2) and B = [K/2, K), each padded to kSortedMaxCols and
+// sorted in LDS in turn with its own chunk bases.  The sorted sample weights of both
+// halves go to the caller's workspace (B's keys pass through it while A is sorted), and
+// the rounds keep both halves' keys and chunk bases in LDS:
+//   [Smem][keys A: kh floats][keys B: kh floats][chunk bases A, B: 2 x 2 x 257 fp64]
+// A cluster's Eq. 23 sums are the sums over the two halves: each switch point is
+// searched in both, and a prefix sum is P_A + P_B at the two indices, the in-chunk
+// weights read from the workspace.  Workspace per row: keys B, weights A, weights B,
+// kh floats each.
+constexpr int kSortedChunkMax = kSortedMaxCols / kSortedThreads;  // chunk length bound
+__device__ __forceinline__ void half_prefix(const float* key, const float* wt_g, const double* tot, int n, int at,
+                                            double& q0, double& q1) {
+  // chunk base at `at`, then the chunk's elements before `at` in order; the weights come
+  // from global memory, all loads issued first (indices clamped into the half)
+  const int C = (n + kSortedThreads - 1) / kSortedThreads;
+  const int ch = min(at / C, kSortedThreads);
+  const int base = ch * C;
+  q0 = tot[ch];
+  q1 = tot[kSortedTB + ch];
+  float wv[kSortedChunkMax];
+#pragma unroll
+  for (int j = 0; j < kSortedChunkMax; ++j) wv[j] = wt_g[min(base + j, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kSortedChunkMax; ++j) {
+    if (base + j < at) {
+      const double av = wv[j];
+      q0 += av;
+      q1 += av * static_cast<double>(key[base + j]);
     }
-    wave_lds_fence();
+  }
+}
+
+__global__ __launch_bounds__(kSortedThreads) void sorted_lloyd_split_kernel(const SortedDesc d) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
+  constexpr int kh = kSortedMaxCols;
+  const int K = d.n_cols, KA = K / 2, KB = K - KA, k = d.n_clusters, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  float* key = reinterpret_cast<float*>(smem_raw + kSmemHdr);  // [2 kh]
+  double* totA = reinterpret_cast<double*>(key + 2 * kh);      // [2][257]
+  double* totB = totA + 2 * kSortedTB;
+  const int64_t row = blockIdx.x;
+  const float* ws = d.w_s + row * K;
+  const float* ar = d.a + row * K;
+  float* keyB_g = d.work + row * (3 * static_cast<int64_t>(kh));
+  float* wtA_g = keyB_g + kh;
+  float* wtB_g = wtA_g + kh;
+  if (tid < k) S.c[tid] = d.c_in[row * k + tid];
+  // half B: sort in the whole key area (keys, then weights), bases, out to the workspace
+  for (int i = tid; i < kh; i += kSortedThreads) {
+    key[i] = i < KB ? ws[KA + i] : __builtin_huge_valf();
+    key[kh + i] = i < KB ? ar[KA + i] : 0.0f;
+  }
+  __syncthreads();
+  sort_pairs<kSortedMaxCols / 2 / kSortedThreads>(key, key + kh, kh, tid);
+  chunk_bases(key, key + kh, KB, totB, tid);
+  for (int i = tid; i < KB; i += kSortedThreads) {
+    keyB_g[i] = key[i];
+    wtB_g[i] = key[kh + i];
+  }
+  __syncthreads();
+  // half A: the same, its keys stay in the first half of the area
+  for (int i = tid; i < kh; i += kSortedThreads) {
+    key[i] = i < KA ? ws[i] : __builtin_huge_valf();
+    key[kh + i] = i < KA ? ar[i] : 0.0f;
+  }
+  __syncthreads();
+  sort_pairs<kSortedMaxCols / 2 / kSortedThreads>(key, key + kh, kh, tid);
+  chunk_bases(key, key + kh, KA, totA, tid);
+  for (int i = tid; i < KA; i += kSortedThreads) wtA_g[i] = key[kh + i];
+  __syncthreads();  // every weight of A is read before B's keys replace them
+  for (int i = tid; i < KB; i += kSortedThreads) key[kh + i] = keyB_g[i];
+  __syncthreads();  // also orders this workgroup's workspace stores before the rounds' loads
+  const float* keyA = key;
+  const float* keyB = key + kh;
+  // the rounds run on wave 0 alone (no block barrier from here on)
+  if (tid >= kWave) return;
+  const float off = d.symmetric ? static_cast<float>(k / 2) : 0.0f;
+  const int G = kCellsPerUnit * k;
+  float sv, t;
+  int si;
+  uint32_t tc;
+  int U = build_structure(S, k, G, off, lane, t, tc, sv, si);
+  for (int it = 0; it < d.iters; ++it) {
+    int ia = KA, ib = KB;
+    if (lane + 1 < U) {
+      const float th = S.thr[lane];
+      ia = keys_below(keyA, KA, th);
+      ib = keys_below(keyB, KB, th);
+    }
+    double q0 = 0.0, q1 = 0.0;
+    if (lane < U) {
+      double a0, a1, b0, b1;
+      half_prefix(keyA, wtA_g, totA, KA, ia, a0, a1);
+      half_prefix(keyB, wtB_g, totB, KB, ib, b0, b1);
+      q0 = a0 + b0;
+      q1 = a1 + b1;
+    }
+    publish_position_sums(S, lane, U, q0, q1);
     bool same;
     U = update_and_structure(S, 1, k, G, off, lane, U, sv, si, t, tc, same);
   }
@@ -312,13 +438,27 @@ hipError_t launch_restart_merge(const MergeDesc& d, hipStream_t stream) {
 }
 
 size_t sorted_lloyd_lds_bytes(int64_t n_cols) {
+  if (n_cols > kSortedMaxCols)  // two halves: both halves' keys and chunk bases
+    return kSmemHdr + 2 * sizeof(float) * static_cast<size_t>(kSortedMaxCols) +
+           4 * sizeof(double) * (kSortedThreads + 1);
   int64_t kp = 2;
   while (kp < n_cols) kp <<= 1;
   return kSmemHdr + 2 * sizeof(float) * static_cast<size_t>(kp) + 2 * sizeof(double) * (kSortedThreads + 1);
 }
 
+size_t sorted_lloyd_work_bytes(int64_t n_rows, int64_t n_cols) {
+  return n_cols > kSortedMaxCols ? static_cast<size_t>(n_rows) * 3 * sizeof(float) * kSortedMaxCols : 0;
+}
+
 hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
   if (d.n_rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(d.n_rows));
+  if (d.n_cols > kSortedMaxCols) {
+    d.kp = kSortedMaxCols;
+    hipLaunchKernelGGL(sorted_lloyd_split_kernel, grid, dim3(kSortedThreads), sorted_lloyd_lds_bytes(d.n_cols),
+                       stream, d);
+    return hipGetLastError();
+  }
   int kp = 2;
   while (kp < d.n_cols) kp <<= 1;
   d.kp = kp;
@@ -326,7 +466,6 @@ hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream) {
   // sized for them); longer rows up to kSortedMaxCols the one with 32
   constexpr int kSmallCols = kSortedThreads * kSortedRegs;
   static_assert(kSortedMaxCols == 4 * kSmallCols, "the large instance covers 4x the small one");
-  const dim3 grid(static_cast<unsigned>(d.n_rows));
   if (kp <= kSmallCols)
     hipLaunchKernelGGL((sorted_lloyd_kernel<kSmallCols / 2 / kSortedThreads>), grid, dim3(kSortedThreads),
                        sorted_lloyd_lds_bytes(d.n_cols), stream, d);

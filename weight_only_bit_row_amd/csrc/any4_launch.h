@@ -94,14 +94,16 @@ hipError_t launch_pack(const MatDesc& m, int group, int n_clusters, const uint8_
 // Sorted-row Lloyd rounds behind any4_stage_lloyd_sorted: from the scaled rows w_s and
 // sample weights a ([n_rows, n_cols] fp32 each) and the centroids c_in [n_rows, k], run
 // `iters` rounds and write c_out [n_rows, k].  One 256-lane workgroup per row, the row
-// sorted in LDS (8 bytes per padded column: 128 KB at 16384), so rows hold at most
-// kSortedMaxCols columns.
+// sorted in LDS (8 bytes per padded column: 128 KB at 16384) for rows of at most
+// kSortedMaxCols columns; longer rows, up to twice that, are sorted as two halves in turn
+// and keep their sorted sample weights in `work` (sorted_lloyd_work_bytes).
 constexpr int kSortedMaxCols = 16384;
 struct SortedDesc {
   const float* w_s;
   const float* a;
   const float* c_in;
   float* c_out;
+  float* work;         // rows past kSortedMaxCols: 3 x kSortedMaxCols floats per row
   int64_t n_rows;
   int32_t n_cols;
   int32_t kp;          // n_cols rounded up to a power of two (set by the launcher)
@@ -111,6 +113,7 @@ struct SortedDesc {
   int32_t pad_;
 };
 size_t sorted_lloyd_lds_bytes(int64_t n_cols);
+size_t sorted_lloyd_work_bytes(int64_t n_rows, int64_t n_cols);
 hipError_t launch_sorted_lloyd(SortedDesc d, hipStream_t stream);
 
 // Restarts: after restart r has written its outputs to the `cand_*` buffers, keep them
