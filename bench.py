@@ -364,13 +364,13 @@ def gpu_config(any4, torch, wl, dev, stream, steps=10, warmup=2):
     def med(n_iters, n):
         for _ in range(warmup):
             any4.quantize_batch(items, group=g, n_clusters=k, iters=n_iters, outputs=outs, ws=ws,
-                                matrix_indices=idx)
+                                matrix_indices=idx, variant=any4.ALL_ROUNDS)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for e0, e1 in evs:
             e0.record(stream)
             any4.quantize_batch(items, group=g, n_clusters=k, iters=n_iters, outputs=outs, ws=ws,
-                                matrix_indices=idx)
+                                matrix_indices=idx, variant=any4.ALL_ROUNDS)
             e1.record(stream)
         torch.cuda.synchronize()
         return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
@@ -483,7 +483,7 @@ def main():
         outs = any4.quantize_batch(items, group=g, n_clusters=k, iters=p_iters, matrix_indices=idx)
         for _ in range(args.profile_steps):
             any4.quantize_batch(items, group=g, n_clusters=k, iters=p_iters, outputs=outs,
-                                matrix_indices=idx)
+                                matrix_indices=idx, variant=any4.ALL_ROUNDS)
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": head_name}))
         return
@@ -507,7 +507,7 @@ def main():
     if args.profile_steps:
         p_iters = iters if args.iters is None else args.iters
         for _ in range(args.profile_steps):
-            any4.quantize(w, act, group=g, n_clusters=k, iters=p_iters, out=out, ws=ws)
+            any4.quantize(w, act, group=g, n_clusters=k, iters=p_iters, out=out, ws=ws, variant=any4.ALL_ROUNDS)
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": head_name,
                           "status": any4.read_status(ws)}))
@@ -515,16 +515,20 @@ def main():
 
     stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
 
-    def timed(n_iters, steps, warmup):
+    # Every timed call runs all `iters` Lloyd rounds (ANY4_ALL_ROUNDS): without it a row
+    # stops at an exact fixed point of its centroids, with the same output bits, and the
+    # credited work would count rounds that did not run.  The stopping form is timed
+    # after the headline steps, beside `value`.
+    def timed(n_iters, steps, warmup, variant=any4.ALL_ROUNDS):
         for _ in range(warmup):
-            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws)
+            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws, variant=variant)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         t0 = time.perf_counter()
         for e0, e1 in evs:
             e0.record(stream)
-            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws)
+            any4.quantize(w, act, group=g, n_clusters=k, iters=n_iters, out=out, ws=ws, variant=variant)
             e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -534,6 +538,7 @@ def main():
     wall, ms = timed(iters, args.steps, args.warmup)
     status = any4.read_status(ws)
     _, ms0 = timed(0, max(5, args.steps // 2), 2)
+    _, ms_stop = timed(iters, max(5, args.steps // 2), 2, variant=0)
     ms_step = wall * 1e3 / args.steps
     ms_kernel = float(np.mean(ms))
     t20, t0_ = float(np.median(ms)), float(np.median(ms0))
@@ -564,6 +569,7 @@ def main():
         "lloyd_pct_fp32_peak_credited": (elem_iters * (3 * k + 1) / ((t20 - t0_) * 1e-3) / 1e12
                                          / PEAK_FP32_TFLOPS * 100) if t20 > t0_ else None,
         "ms_iters0": t0_,
+        "ms_per_matrix_fixed_point_stop": float(np.median(ms_stop)),
         "device_status": status,
         "roofline": {
             "bound": "alu",

@@ -97,7 +97,12 @@ enum {
   ANY4_INIT_KMEANSPP = 0, ANY4_INIT_RANDOM = 1 << 2, ANY4_INIT_UNIFORM = 2 << 2,
   ANY4_INIT_GREEDY = 3 << 2,
   /* symmetric scaling (Section 2.5.1, Eq. 3): alpha = max|w| / 2^(n-1), beta = 0 */
-  ANY4_SCALE_SYMMETRIC = 1 << 4
+  ANY4_SCALE_SYMMETRIC = 1 << 4,
+  /* not a method variant: run every one of `iters` Lloyd rounds.  By default a row stops
+   * once a round leaves every centroid's bits unchanged, since each later round would
+   * give the same assignment, sums and centroids again; the outputs are the same bits
+   * either way, only the time differs. */
+  ANY4_ALL_ROUNDS = 1 << 5
 };
 /* restarts (n_init): the whole k-means runs from n initializations (restart r draws
  * from Philox counters t + 16 r) and each row keeps the run with the lowest final
@@ -109,8 +114,8 @@ enum {
  *             the paper's default)
  * n_clusters: 2, 4, 8 or 16 (any1..any4; Qmax - Qmin = n_clusters - 1)
  * iters:      Lloyd rounds (E-step then M-step), >= 0, followed by one final E-step
- * variant:    0, or ANY4_WEIGHT_* | ANY4_INIT_* | ANY4_SCALE_SYMMETRIC | ANY4_RESTARTS(n);
- *             any other bit is an invalid argument
+ * variant:    0, or ANY4_WEIGHT_* | ANY4_INIT_* | ANY4_SCALE_SYMMETRIC | ANY4_RESTARTS(n),
+ *             optionally with ANY4_ALL_ROUNDS; any other bit is an invalid argument
  * seed:       Philox4x32-10 key for k-means++ and random initialization */
 typedef struct {
   int32_t group;

@@ -125,6 +125,9 @@ def oracle_row_inputs(w_row, dtype, act, g, k, variant=0):
     return ws, a
 
 
+ALL_ROUNDS = 1 << 5  # the library's ANY4_ALL_ROUNDS: every Lloyd round, no stop at a fixed point
+
+
 def explain_gpu_row(any4, w_row, dtype, act, g, k, iters, seed, row_offset, matrix_index, variant,
                     gpu_codes_row):
     """explain_divergence for one row of a GPU quantization: the row is re-run on its own
@@ -134,8 +137,9 @@ def explain_gpu_row(any4, w_row, dtype, act, g, k, iters, seed, row_offset, matr
     assert (variant >> 8) == 0, "with restarts every row must be identical"
     o = _oracle()
     w1 = np.ascontiguousarray(np.asarray(w_row)[None, :])
+    # the oracle runs every round anyway: the no-early-stop bit is not a method variant
     ref = o.quantize(w1, dtype, act, g, k, iters, seed=seed, row_offset=row_offset,
-                     matrix_index=matrix_index, trace=True, variant=variant)
+                     matrix_index=matrix_index, trace=True, variant=variant & ~ALL_ROUNDS)
     ws, a = oracle_row_inputs(w_row, dtype, act, g, k, variant)
 
     class _M:

@@ -55,8 +55,10 @@ int main() {
   any4_matrix longrow = mat(4, 65536);
   EXPECT(any4_workspace_bytes(&longrow, 1, &p, &bytes), ANY4_ERR_UNSUPPORTED);
   any4_params var = p;
-  var.variant = 1 << 5;
+  var.variant = 1 << 6;
   EXPECT(any4_workspace_bytes(&m, 1, &var, &bytes), ANY4_ERR_INVALID_ARG);
+  var.variant = ANY4_ALL_ROUNDS;
+  EXPECT(any4_workspace_bytes(&m, 1, &var, &bytes), ANY4_OK);
 
   // a mixed batch: 12 matrices over every row geometry, with and without restarts
   std::vector<any4_matrix> batch;

@@ -187,6 +187,19 @@ def test_t4_many_rounds_fixed_point_stop(shape):
     for i in np.nonzero(fixed & same_rows)[0]:
         assert np.array_equal(c_more[i].view(np.uint32), c_final.cpu().numpy()[i].view(np.uint32)), (name, i)
     say(f"  {name}: rows identical {same_rows.mean():.3f}, at a fixed point {fixed.mean():.3f}")
+    # every round run, no stop at the fixed point: the same bar against the oracle, and
+    # the same bits as the stopping run on every row that the tests have seen
+    out_a, c_a, picks_a, ws_a = any4().stage_full(w, act, group=g, n_clusters=k, iters=iters, seed=0,
+                                                  variant=any4().ALL_ROUNDS)
+    torch.cuda.synchronize()
+    assert any4().read_status(ws_a) == 0
+    assert np.array_equal(picks_a.cpu().numpy(), ref["picks"])
+    codes_a, c_a = out_a.codes.cpu().numpy(), c_a.cpu().numpy()
+    check_rows(any4(), m, g, k, iters, 0, codes_a, c_a, out_a.lut.cpu().numpy().view(np.uint16), ref,
+               np.arange(N), variant=any4().ALL_ROUNDS)
+    same_bits = np.all(codes_a == out.codes.cpu().numpy(), axis=1) & \
+        np.all(c_a.view(np.uint32) == c_final.cpu().numpy().view(np.uint32), axis=1)
+    say(f"  {name}: all rounds vs stopping run, rows with the same bits {same_bits.mean():.3f}")
 
 
 def test_t6_repeat_and_row_shards(case):

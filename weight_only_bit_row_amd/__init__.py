@@ -20,6 +20,7 @@ ANY4_F32, ANY4_BF16 = 0, 1
 WEIGHT_ALPHA_ACT, WEIGHT_ACT, WEIGHT_NONE = 0, 1, 2
 INIT_KMEANSPP, INIT_RANDOM, INIT_UNIFORM, INIT_GREEDY = 0, 1 << 2, 2 << 2, 3 << 2
 SCALE_SYMMETRIC = 1 << 4
+ALL_ROUNDS = 1 << 5   # every Lloyd round, no stop at an exact fixed point (same output bits)
 
 
 def RESTARTS(n: int) -> int:

@@ -127,7 +127,8 @@ LaunchArgs make_args(const any4_params* p, int nw, uint32_t* status) {
   a.n_clusters = p->n_clusters;
   a.iters = p->iters;
   a.nw = nw;
-  a.variant = p->variant & ((1 << any4::kVarRestartShift) - 1);
+  a.variant = p->variant & ((1 << any4::kVarRestartShift) - 1) & ~any4::kVarAllRounds;
+  a.all_rounds = (p->variant & any4::kVarAllRounds) ? 1 : 0;
   a.restart = 0;
   a.seed = p->seed;
   a.status = status;

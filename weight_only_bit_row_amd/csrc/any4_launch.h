@@ -42,8 +42,9 @@ struct MatDesc {
 constexpr int32_t kVarWeightMask = 0x3;       // sample weights: 0 alpha*E|x|, 1 E|x|, 2 none
 constexpr int32_t kVarInitShift = 2;          // init: 0 k-means++, 1 random, 2 uniform levels
 constexpr int32_t kVarSymmetric = 1 << 4;     // Eq. 3 scaling
+constexpr int32_t kVarAllRounds = 1 << 5;     // no stop at a fixed point (not a method variant)
 constexpr int32_t kVarRestartShift = 8;       // bits 8-15: restarts - 1
-constexpr int32_t kVarKnownBits = 0xFF1F;
+constexpr int32_t kVarKnownBits = 0xFF3F;
 enum : int32_t { INIT_KMEANSPP = 0, INIT_RANDOM = 1, INIT_UNIFORM = 2, INIT_GREEDY = 3 };
 
 struct LaunchArgs {
@@ -58,7 +59,7 @@ struct LaunchArgs {
   uint64_t seed;
   uint32_t* status;                 // device status word or NULL
   int32_t restart;                  // the Philox counter's second word is t + 16 * restart
-  int32_t pad_;
+  int32_t all_rounds;               // run every round, no stop at an exact fixed point
 };
 
 // Row-kernel launch geometry for a row length: elements per lane E and waves per row.

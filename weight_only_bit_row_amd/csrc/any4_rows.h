@@ -1499,7 +1499,7 @@ void any4_rows_kernel(const LaunchArgs args) {
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
     // a fixed point: the remaining rounds would reproduce these centroids bit for bit
-    if (S.done != 0) break;
+    if (S.done != 0 && !args.all_rounds) break;
   }
   if (MODE == MODE_STEP) {
     if (tid < k) M.c_out[row * k + tid] = S.c[tid];
