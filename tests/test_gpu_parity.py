@@ -419,11 +419,13 @@ def test_layer_batch_sampled_rows(bits):
             f"dJ/J {dj:.2e}")
 
 
-# Rows of 5-16 waves sum the Eq. 23 terms in 64-bit fixed point scaled to the row's
+# Rows of 2-16 waves sum the Eq. 23 terms in 64-bit fixed point scaled to the row's
 # largest sample weight.  Weights spread over 2^40 (a tenth of the channels scaled by
 # 2^-28, one in a hundred by 2^12) must still give the oracle's rounds and codes, also
 # under symmetric scaling, where w_S and so the S1 terms are negative.
-WIDE_SPAN = [("five_waves_k10240", 4, 10240, BF16, 128, 16, 51, 0),
+WIDE_SPAN = [("two_waves_k4096", 6, 4096, BF16, 128, 16, 54, 0),
+             ("three_waves_symmetric_any3_k6144", 4, 6144, BF16, 64, 8, 55, 1 << 4),
+             ("five_waves_k10240", 4, 10240, BF16, 128, 16, 51, 0),
              ("fourteen_waves_k28672", 2, 28672, BF16, 128, 16, 52, 0),
              ("seven_waves_symmetric_k14336", 3, 14336, BF16, 128, 16, 53, 1 << 4)]
 

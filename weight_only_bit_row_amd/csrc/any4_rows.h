@@ -29,9 +29,9 @@
 //              table would need a second switch point in one cell uses a 4-level
 //              binary search over all switch points instead (same result).  The
 //              element then adds (a_j, a_j*w_S_j) in fp64 (the product is exact) into
-//              lane-private LDS bins, reduced per wave in a fixed order; rows of 5-16
-//              waves add the same terms in 64-bit fixed point (exact integer sums) into
-//              one set of bins for the whole row (no global atomics)
+//              lane-private LDS bins, reduced in a fixed order (one-wave rows); rows of
+//              2-16 waves add the same terms in 64-bit fixed point (exact integer sums)
+//              into one set of bins for the whole row (no global atomics)
 //   emit       final assignment, nibble packing, fp16 LUT/scale/offset, fp64 objective
 //
 // All float code is compiled with -ffp-contract=off: every squared distance is
@@ -200,7 +200,7 @@ __device__ __forceinline__ unsigned long long exact_u64(double v) {
   return static_cast<unsigned long long>(__double_as_longlong(v + 4503599627370496.0)) -
          0x4330000000000000ull;
 }
-// Fixed-point Eq. 23 terms (rows of 5-16 waves): a term t with |t| < 2^51 becomes the
+// Fixed-point Eq. 23 terms (rows of 2-16 waves): a term t with |t| < 2^51 becomes the
 // nearest integer by one fused add of 1.5 * 2^52, whose result lies in [2^52, 2^53) where
 // doubles are spaced by 1; the bit pattern of that double minus the constant's is the
 // integer in two's complement (one op on the high word).  Integer sums do not depend on
@@ -1405,11 +1405,11 @@ void any4_rows_kernel(const LaunchArgs args) {
 #pragma unroll
   for (int m = 0; m < E; ++m)
     cw[m / kCellsPerWord] |= (cell_of(xv[m], G, cell_off) * kCellBytes) << (8 * (m % kCellsPerWord));
-  // Rows of 5-16 waves sum the Eq. 23 terms in 64-bit fixed point, all waves into one
+  // Rows of 2-16 waves sum the Eq. 23 terms in 64-bit fixed point, all waves into one
   // set of bins (wave 0's area), which wave 0 alone reduces after the round's first
-  // barrier: one 8 KB reduction per round instead of one per wave.  Shorter rows keep
-  // per-wave fp64 bins, reduced by every wave before that barrier.
-  constexpr bool FIX = NWMAX > 8;
+  // barrier: one 8 KB reduction per round instead of one per wave.  One-wave rows keep
+  // fp64 bins, reduced before that barrier.
+  constexpr bool FIX = NWMAX > 1;
   double* bins = reinterpret_cast<double*>(smem_raw + kSmemHdr + kTableBytes) +
                  (FIX ? 0 : wave) * (2 * kMaxClusters * kBinCols);
   // Fixed-point scale: a * 2^sigma < 2^43 for every sample weight of the row (exact, a
