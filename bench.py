@@ -40,9 +40,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # the row kernel's source: its device code and the translation unit of the instance the
-# headline workload runs (32 elements per lane, up to 8 waves)
+# headline workload runs (32 elements per lane, the 1024-lane instance)
 KERNEL_SRC = (os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_rows.h"),
-              os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_rows_e32_w8.hip"))
+              os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_rows_e32_w16.hip"))
 COUNTERS = os.path.join(ROOT, "profiles", "any4_rows_up_proj_counters.md")
 BOOKENDS_SRC = os.path.join(ROOT, "weight_only_bit_row_amd", "csrc", "any4_bookends.hip")
 BOOKENDS_COUNTERS = os.path.join(ROOT, "profiles", "any4_bookends_calib32x2048_up_proj.md")
