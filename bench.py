@@ -561,7 +561,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "Llama3-8B-like up_proj 14336x4096 bf16, group 128, 16 clusters, "
-                               "20 Lloyd rounds, Philox seed 0",
+                               "20 Lloyd rounds, every one run (ANY4_ALL_ROUNDS), Philox seed 0",
                    "n_rows": N, "n_cols": K, "group": g, "n_clusters": k, "iters": iters},
         "ms_per_matrix": t20,
         "lloyd_ms": t20 - t0_,
