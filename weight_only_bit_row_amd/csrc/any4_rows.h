@@ -933,8 +933,8 @@ struct WavesPerEU {
 // The variant instance for narrow groups is held to 2 waves per SIMD instead of 3: at
 // 168 VGPRs it spilled ~3700 registers around the narrow-group scaling cases; at 2 waves
 // it spills none and runs 17-35% faster (group 8 and 16 variants on 14336 x 4096).
-// The 1024-lane instance (NWMAX 16, rows of 5 to 16 waves) is capped at 128 VGPRs: such a
-// workgroup may put 4 waves on every SIMD.
+// The 1024-lane instance (NWMAX 16: rows of 5 to 16 waves, and default-path rows of 2 to 4
+// waves) is capped at 128 VGPRs: such a workgroup may put 4 waves on every SIMD.
 template <int E, int NWMAX, int MODE, bool WIDE, bool VAR>
 __global__ __launch_bounds__(kWave* NWMAX)
 __attribute__((amdgpu_waves_per_eu(NWMAX > 8 ? 4

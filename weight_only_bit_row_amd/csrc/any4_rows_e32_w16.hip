@@ -1,4 +1,6 @@
-// Row-kernel instance: 32 elements per lane, 5-16 waves per row (8193-32768 columns).
+// Row-kernel instance: 32 elements per lane, up to 16 waves per row at up to 128 VGPRs (the
+// 1024-lane instance): rows of 5-16 waves (8193-32768 columns), and on the default path
+// also rows of 2-4 waves (2049-8192 columns), eight 2-wave rows per CU.
 #include "any4_rows.h"
 
 namespace any4 {

@@ -1,7 +1,8 @@
-// Row-kernel instance: 32 elements per lane, 2-4 waves per row (2049-8192 columns).
-// Its element passes take their elements in chunks of 16 (table reads in flight
-// together): with the fixed-point bins this instance then spills nothing in the default
-// path, against 16 bytes per lane with chunks of 8, and the rounds run ~2% faster.
+// Row-kernel instance: 32 elements per lane, 2-4 waves per row (2049-8192 columns), at
+// up to 168 VGPRs; rows with a method variant run here (the default path's rows of 2-4
+// waves run on the 1024-lane instance).  Its element passes take their elements in
+// chunks of 16 (table reads in flight together): with the fixed-point bins the default
+// instance then spills nothing, against 16 bytes per lane with chunks of 8.
 #define ANY4_CHUNK 16
 #include "any4_rows.h"
 
